@@ -1,0 +1,427 @@
+"""Pins for the fp64 oracle: each test ties it to something other than itself.
+
+Closed forms, special cases, brute force and an independent library routine (torch's CPU
+float64 scaled_dot_product_attention). Every mistake of the usual kind -- a dropped scale, a
+mask off by one, a wrong GQA head map, a transposed operand, a wrong block/slot split --
+fails at least one of these (test_mutants_are_caught plants such mistakes in copies).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import bf16_value, bf16_bits, context_lens, paged_table, WORKLOADS
+
+RNG = np.random.default_rng(12345)
+
+
+def _rand(*shape, rng=RNG):
+    return rng.standard_normal(shape)
+
+
+# --- P1: normalisation -------------------------------------------------------------------
+@pytest.mark.parametrize("causal,window", [(True, 0), (True, 3), (False, 0), (False, 2)])
+def test_ones_v_gives_ones(causal, window):
+    """V == 1 => O == 1: the softmax weights of every row sum to one."""
+    q, k = _rand(2, 7, 4, 8), _rand(2, 7, 2, 8)
+    v = np.ones((2, 7, 2, 8))
+    o, _ = oracle.attention(q, k, v, 0.3, causal, window)
+    assert np.abs(o - 1).max() < 1e-14
+
+
+def test_lse_closed_form():
+    """lse is log(sum exp s) of the visible scores (2 keys, hand-set scores 0 and ln 3)."""
+    k = np.array([[1.0, 0.0], [0.0, 1.0]])
+    q = np.array([[0.0, math.log(3.0)]])
+    v = np.array([[4.0, 0.0], [0.0, 8.0]])
+    o, lse = oracle.attention_head(q, k, v, 1.0, [1], causal=True)
+    # weights 1/4 and 3/4
+    assert np.allclose(o, [[1.0, 6.0]], atol=1e-15)
+    assert abs(lse[0] - math.log(4.0)) < 1e-15
+
+
+# --- P2: single visible key ---------------------------------------------------------------
+def test_single_key_rows():
+    """Prefill row 0 sees only key 0: O = V[0] of the mapped KV head, exactly."""
+    q, k, v = _rand(1, 5, 6, 4), _rand(1, 5, 3, 4), _rand(1, 5, 3, 4)
+    o, lse = oracle.attention(q, k, v, 0.5, causal=True)
+    for h in range(6):
+        assert np.array_equal(o[0, 0, h], v[0, 0, h // 2])
+        assert lse[0, h, 0] == pytest.approx(0.5 * q[0, 0, h] @ k[0, 0, h // 2], abs=1e-15)
+
+
+def test_decode_ctx1_returns_v():
+    q = _rand(3, 4, 8)
+    kp, vp = _rand(5, 2, 4, 8), _rand(5, 2, 4, 8)
+    table = np.array([[3, -1], [0, -1], [4, -1]], np.int32)
+    o, _ = oracle.decode_paged(q, kp, vp, table, np.array([1, 1, 1]), 0.1, 4)
+    for b, pb in enumerate([3, 0, 4]):
+        for h in range(4):
+            assert np.array_equal(o[b, h], vp[pb, h // 2, 0])
+
+
+# --- P3: uniform scores -> mean of the visible V rows -------------------------------------
+@pytest.mark.parametrize("window", [0, 1, 3, 100])
+def test_zero_query_gives_window_mean(window):
+    S = 9
+    v = _rand(1, S, 1, 3)
+    q, k = np.zeros((1, S, 1, 3)), _rand(1, S, 1, 3)
+    o, _ = oracle.attention(q, k, v, 1.0, True, window)
+    for i in range(S):
+        lo = 0 if window == 0 else max(0, i - window + 1)
+        assert np.allclose(o[0, i, 0], v[0, lo:i + 1, 0].mean(axis=0), atol=1e-14)
+
+
+# --- P4: window edge ------------------------------------------------------------------------
+def test_window_one_is_identity_and_wide_window_is_causal():
+    q, k, v = _rand(2, 6, 2, 5), _rand(2, 6, 2, 5), _rand(2, 6, 2, 5)
+    o1, _ = oracle.attention(q, k, v, 0.7, True, 1)
+    assert np.array_equal(o1, v)
+    ow, _ = oracle.attention(q, k, v, 0.7, True, 6)
+    oc, _ = oracle.attention(q, k, v, 0.7, True, 0)
+    assert np.abs(ow - oc).max() < 1e-15
+
+
+# --- P5: GQA == MHA with repeated KV heads -------------------------------------------------
+def test_gqa_equals_repeated_mha():
+    q, k, v = _rand(2, 7, 8, 4), _rand(2, 7, 2, 4), _rand(2, 7, 2, 4)
+    og, _ = oracle.attention(q, k, v, 0.4, True, 3)
+    om, _ = oracle.attention(q, np.repeat(k, 4, axis=2), np.repeat(v, 4, axis=2), 0.4, True, 3)
+    assert np.abs(og - om).max() < 1e-15
+
+
+# --- P6 / P7: paged layout ------------------------------------------------------------------
+def _paged_case(seed, bs, spare, permute, B=3, Hkv=2, D=4, ctx=(5, 1, 11)):
+    rng = np.random.default_rng(seed)
+    ctx = np.array(ctx[:B], np.int32)
+    table, nb = paged_table(ctx, bs, seed, spare, permute)
+    kp, vp = rng.standard_normal((nb, Hkv, bs, D)), rng.standard_normal((nb, Hkv, bs, D))
+    return ctx, table, kp, vp
+
+
+def _contiguous_from_paged(pool, table, ctx, bs):
+    """Inverse view built by scanning pool slots (independent of gather_logical)."""
+    out = []
+    for b in range(len(ctx)):
+        rows = []
+        for t in range(int(ctx[b])):
+            hits = [(pb, off) for pb in range(pool.shape[0]) for off in range(bs)
+                    if table[b][t // bs] == pb and off == t - bs * (t // bs)]
+            assert len(hits) == 1
+            rows.append(pool[hits[0][0], :, hits[0][1]])
+        out.append(np.array(rows))
+    return out
+
+
+@pytest.mark.parametrize("bs", [1, 2, 3, 4])
+def test_paged_equals_contiguous_any_permutation(bs):
+    q = _rand(3, 4, 4)
+    outs = []
+    for permute, seed in ((False, 1), (True, 2), (True, 3)):
+        ctx, table, kp, vp = _paged_case(seed, bs, 2, permute)
+        # same logical contents under every table: write logical rows through the table
+        rng = np.random.default_rng(99)
+        logical_k = [rng.standard_normal((int(c), 2, 4)) for c in ctx]
+        logical_v = [rng.standard_normal((int(c), 2, 4)) for c in ctx]
+        for b in range(3):
+            for t in range(int(ctx[b])):
+                kp[table[b][t // bs], :, t % bs] = logical_k[b][t]
+                vp[table[b][t // bs], :, t % bs] = logical_v[b][t]
+        o, _ = oracle.decode_paged(q, kp, vp, table, ctx, 0.3, bs)
+        outs.append(o)
+        # contiguous reference per sequence, from the slot-scanning inverse view
+        kc = _contiguous_from_paged(kp, table, ctx, bs)
+        vc = _contiguous_from_paged(vp, table, ctx, bs)
+        for b in range(3):
+            oc, _ = oracle.attention(q[b][None, None], kc[b][None], vc[b][None], 0.3, True)
+            assert np.abs(o[b] - oc[0, 0]).max() < 1e-14
+    assert np.abs(outs[0] - outs[1]).max() < 1e-14
+    assert np.abs(outs[0] - outs[2]).max() < 1e-14
+
+
+def test_poisoned_unused_slots_never_read():
+    bs = 4
+    ctx, table, kp, vp = _paged_case(7, bs, 3, True)
+    q = _rand(3, 4, 4)
+    o_ref, _ = oracle.decode_paged(q, kp, vp, table, ctx, 0.3, bs)
+    used = {(int(table[b][t // bs]), t % bs) for b in range(3) for t in range(int(ctx[b]))}
+    for pb in range(kp.shape[0]):
+        for off in range(bs):
+            if (pb, off) not in used:
+                kp[pb, :, off] = np.nan
+                vp[pb, :, off] = np.nan
+    o, _ = oracle.decode_paged(q, kp, vp, table, ctx, 0.3, bs)
+    assert np.isfinite(o).all() and np.array_equal(o, o_ref)
+
+
+def test_window_left_blocks_never_read():
+    """Blocks wholly left of the window may hold anything (table entries too)."""
+    bs, W = 4, 5
+    ctx, table, kp, vp = _paged_case(8, bs, 0, True, ctx=(13, 9, 11))
+    q = _rand(3, 4, 4)
+    o_ref, _ = oracle.decode_paged(q, kp, vp, table, ctx, 0.3, bs, window=W)
+    kp2, vp2 = kp.copy(), vp.copy()
+    for b in range(3):
+        first_visible = int(ctx[b]) - W
+        for t in range(first_visible):
+            kp2[table[b][t // bs], :, t % bs] = np.nan
+            vp2[table[b][t // bs], :, t % bs] = np.nan
+    o, _ = oracle.decode_paged(q, kp2, vp2, table, ctx, 0.3, bs, window=W)
+    assert np.isfinite(o).all() and np.abs(o - o_ref).max() < 1e-14
+
+
+# --- P8: brute force in pure Python -----------------------------------------------------------
+def _brute(q, k, v, scale, causal, window):
+    B, Sq, Hq, D = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    out = np.zeros((B, Sq, Hq, v.shape[3]))
+    for b in range(B):
+        for h in range(Hq):
+            g = h * Hkv // Hq
+            for i in range(Sq):
+                P = Lk - Sq + i
+                keys = [j for j in range(Lk) if (not causal or j <= P) and (window == 0 or P - j < window)]
+                s = [scale * math.fsum(float(q[b, i, h, d]) * float(k[b, j, g, d]) for d in range(D)) for j in keys]
+                m = max(s)
+                e = [math.exp(x - m) for x in s]
+                tot = math.fsum(e)
+                for d in range(v.shape[3]):
+                    out[b, i, h, d] = math.fsum(e[n] * float(v[b, j, g, d]) for n, j in enumerate(keys)) / tot
+    return out
+
+
+@pytest.mark.parametrize("B,Sq,Lk,Hq,Hkv,D,causal,window", [
+    (1, 1, 1, 1, 1, 1, True, 0), (2, 9, 9, 4, 2, 4, True, 0), (2, 9, 9, 4, 2, 3, True, 3),
+    (1, 6, 6, 2, 2, 4, False, 0), (2, 3, 8, 4, 1, 2, True, 0), (1, 1, 7, 4, 2, 4, True, 3),
+    (2, 5, 5, 3, 1, 4, True, 1), (1, 4, 9, 2, 1, 3, False, 4),
+])
+def test_brute_force(B, Sq, Lk, Hq, Hkv, D, causal, window):
+    rng = np.random.default_rng(B * 1000 + Sq * 100 + Lk)
+    q, k, v = rng.standard_normal((B, Sq, Hq, D)), rng.standard_normal((B, Lk, Hkv, D)), rng.standard_normal((B, Lk, Hkv, D))
+    o, _ = oracle.attention(q, k, v, 0.6, causal, window)
+    assert np.abs(o - _brute(q, k, v, 0.6, causal, window)).max() < 1e-12
+
+
+@pytest.mark.parametrize("bs", [1, 2, 3])
+@pytest.mark.parametrize("window", [0, 1, 3])
+def test_brute_force_paged_decode(bs, window):
+    rng = np.random.default_rng(bs * 10 + window)
+    ctx = np.array([5, 2], np.int32)
+    table, nb = paged_table(ctx, bs, 17 + bs, 1, True)
+    kp, vp = rng.standard_normal((nb, 2, bs, 3)), rng.standard_normal((nb, 2, bs, 3))
+    q = rng.standard_normal((2, 4, 3))
+    o, _ = oracle.decode_paged(q, kp, vp, table, ctx, 0.5, bs, window)
+    for b in range(2):
+        n = int(ctx[b])
+        kc = np.array([[kp[table[b][t // bs], g, t % bs] for g in range(2)] for t in range(n)])
+        vc = np.array([[vp[table[b][t // bs], g, t % bs] for g in range(2)] for t in range(n)])
+        ob = _brute(q[b][None, None], kc[None], vc[None], 0.5, True, window)
+        assert np.abs(o[b] - ob[0, 0]).max() < 1e-12
+
+
+# --- P9: prefill last row == decode over the same keys ---------------------------------------
+def test_prefill_last_row_equals_decode():
+    bs, S = 4, 10
+    rng = np.random.default_rng(5)
+    q, k, v = rng.standard_normal((1, S, 4, 8)), rng.standard_normal((1, S, 2, 8)), rng.standard_normal((1, S, 2, 8))
+    op, _ = oracle.attention(q, k, v, 0.35, True, 4)
+    table, nb = paged_table(np.array([S]), bs, 3, 0, True)
+    kp, vp = np.zeros((nb, 2, bs, 8)), np.zeros((nb, 2, bs, 8))
+    for t in range(S):
+        kp[table[0][t // bs], :, t % bs] = k[0, t]
+        vp[table[0][t // bs], :, t % bs] = v[0, t]
+    od, _ = oracle.decode_paged(q[:, -1], kp, vp, table, np.array([S]), 0.35, bs, 4)
+    assert np.abs(op[0, -1] - od[0]).max() < 1e-14
+
+
+# --- P10: split + log-sum-exp merge == unsplit -------------------------------------------------
+@pytest.mark.parametrize("cuts", [(3,), (1, 2, 9), (4, 8, 12)])
+def test_merge_of_splits_equals_whole(cuts):
+    rng = np.random.default_rng(11)
+    Lk, D = 15, 6
+    q, k, v = rng.standard_normal((2, D)), rng.standard_normal((Lk, D)), rng.standard_normal((Lk, D))
+    o, lse = oracle.attention_head(q, k, v, 0.4, [Lk - 1, Lk - 1], causal=True)
+    edges = [0, *cuts, Lk]
+    outs, lses = [], []
+    for a, b in zip(edges[:-1], edges[1:]):
+        if a == b:
+            continue
+        oo, ll = oracle.attention_head(q, k[a:b], v[a:b], 0.4, [b - a - 1] * 2, causal=True)
+        outs.append(oo)
+        lses.append(ll)
+    # an empty split contributes weight zero
+    outs.append(np.zeros_like(o))
+    lses.append(np.full(2, -np.inf))
+    om, lm = oracle.merge_partials(outs, lses)
+    assert np.abs(om - o).max() < 1e-13 and np.abs(lm - lse).max() < 1e-13
+
+
+# --- P11: an independent library routine ------------------------------------------------------
+@pytest.mark.parametrize("S,Hq,Hkv,D,window", [(17, 4, 2, 8, 0), (33, 8, 2, 16, 5), (9, 2, 2, 4, 1)])
+def test_matches_torch_sdpa_float64(S, Hq, Hkv, D, window):
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(S)
+    q, k, v = rng.standard_normal((2, S, Hq, D)), rng.standard_normal((2, S, Hkv, D)), rng.standard_normal((2, S, Hkv, D))
+    o, _ = oracle.attention(q, k, v, 1 / math.sqrt(D), True, window)
+    i = torch.arange(S)[:, None]
+    j = torch.arange(S)[None, :]
+    mask = j <= i
+    if window:
+        mask &= (i - j) < window
+    t = lambda x: torch.from_numpy(x).permute(0, 2, 1, 3)
+    ot = torch.nn.functional.scaled_dot_product_attention(
+        t(q), t(k), t(v), attn_mask=mask, scale=1 / math.sqrt(D), enable_gqa=True)
+    assert np.abs(o - ot.permute(0, 2, 1, 3).numpy()).max() < 1e-12
+
+
+# --- V linearity -------------------------------------------------------------------------------
+def test_linear_in_v():
+    rng = np.random.default_rng(3)
+    q, k = rng.standard_normal((1, 8, 2, 4)), rng.standard_normal((1, 8, 1, 4))
+    v1, v2 = rng.standard_normal((1, 8, 1, 4)), rng.standard_normal((1, 8, 1, 4))
+    o1, _ = oracle.attention(q, k, v1, 0.5, True, 3)
+    o2, _ = oracle.attention(q, k, v2, 0.5, True, 3)
+    o12, _ = oracle.attention(q, k, 2 * v1 - 3 * v2, 0.5, True, 3)
+    assert np.abs(o12 - (2 * o1 - 3 * o2)).max() < 1e-13
+
+
+# --- P12: INT8 quantizer closed forms -----------------------------------------------------------
+def test_int8_hand_values():
+    # absmax 1.27 -> s = fp16(0.01) = 0.01000213623046875; 1.27/s = 126.97 -> 127;
+    # -0.635/s = -63.486 -> -63; 0.005/s = 0.49989 -> 0; 0.015/s = 1.4997 -> 1.
+    x = np.array([[1.27, -0.635, 0.005, 0.015]], np.float32)
+    codes, s = oracle.quantize_int8(x)
+    assert s.dtype == np.float16 and float(s[0]) == 0.01000213623046875
+    assert codes.tolist() == [[127, -63, 0, 1]]
+    # exact halves round to even: s = 1 (absmax 127), 2.5 -> 2, 3.5 -> 4, -0.5 -> 0
+    codes, s = oracle.quantize_int8(np.array([[127.0, 2.5, 3.5, -0.5]], np.float32))
+    assert float(s[0]) == 1.0 and codes.tolist() == [[127, 2, 4, 0]]
+    # the zero vector
+    codes, s = oracle.quantize_int8(np.zeros((1, 4), np.float32))
+    assert float(s[0]) == 0.0 and codes.tolist() == [[0, 0, 0, 0]]
+
+
+def test_int8_error_bound_and_range():
+    rng = np.random.default_rng(21)
+    x = bf16_value(bf16_bits(rng.standard_normal((4096, 128)).astype(np.float32)))
+    codes, s = oracle.quantize_int8(x)
+    s64 = s.astype(np.float64)[:, None]
+    assert codes.min() >= -127 and codes.max() <= 127
+    err = np.abs(x.astype(np.float64) - codes * s64)
+    assert (err <= s64 / 2 * (1 + 1e-6) + 1e-12).all()
+    # the absmax element maps to +-127
+    idx = np.abs(x).argmax(axis=1)
+    assert (np.abs(codes[np.arange(4096), idx]) == 127).all()
+
+
+# --- P13: append placement ---------------------------------------------------------------------
+def test_append_writes_only_its_slots():
+    bs = 3
+    ctx = np.array([7, 4], np.int32)
+    table, nb = paged_table(ctx, bs, 4, 2, True)
+    pool = np.full((nb, 2, bs, 5), 777.0)
+    seq = np.array([0, 1, 0, 1], np.int32)
+    pos = np.array([6, 0, 2, 3], np.int32)
+    rows = np.arange(4 * 2 * 5, dtype=np.float64).reshape(4, 2, 5)
+    out = oracle.append_expected(pool, rows, seq, pos, table, bs)
+    changed = {(pb, off) for pb in range(nb) for off in range(bs) if not (out[pb, :, off] == 777.0).all()}
+    expect = {(int(table[0][2]), 0), (int(table[1][0]), 0), (int(table[0][0]), 2), (int(table[1][1]), 0)}
+    assert changed == expect
+    assert np.array_equal(out[table[0][2], :, 0], rows[0])
+    assert np.array_equal(out[table[1][1], :, 0], rows[3])
+
+
+# --- the pins catch planted mistakes ------------------------------------------------------------
+def _mut_off_by_one(qpos, Lk, causal, window):
+    qpos = np.asarray(qpos, np.int64)[:, None]
+    j = np.arange(Lk)[None, :]
+    vis = np.ones((qpos.shape[0], Lk), bool)
+    if causal:
+        vis &= j < qpos + (qpos == 0)  # diagonal dropped except row 0
+    if window > 0:
+        vis &= (qpos - j) < window
+    return vis
+
+
+def _mut_window_wide(qpos, Lk, causal, window):
+    qpos = np.asarray(qpos, np.int64)[:, None]
+    j = np.arange(Lk)[None, :]
+    vis = np.ones((qpos.shape[0], Lk), bool)
+    if causal:
+        vis &= j <= qpos
+    if window > 0:
+        vis &= (qpos - j) <= window
+    return vis
+
+
+@pytest.mark.parametrize("mutant", [_mut_off_by_one, _mut_window_wide])
+def test_mutants_are_caught(monkeypatch, mutant):
+    import oracle.attn_fp64 as oa
+    monkeypatch.setattr(oa, "visible_mask", mutant)
+    with pytest.raises(AssertionError):
+        test_brute_force(2, 9, 9, 4, 2, 3, True, 3)
+
+
+def test_gqa_head_map_mutant_is_caught(monkeypatch):
+    import oracle.attn_fp64 as oa
+    orig = oa.attention_head
+
+    def attention_mod(q, k, v, scale, causal=True, window=0):
+        B, Sq, Hq, D = q.shape
+        Hkv = k.shape[2]
+        o = np.empty((B, Sq, Hq, v.shape[3]))
+        lse = np.empty((B, Hq, Sq))
+        for b in range(B):
+            for h in range(Hq):
+                g = h % Hkv  # wrong grouping
+                o[b, :, h], lse[b, h] = orig(q[b, :, h], k[b, :, g], v[b, :, g], scale,
+                                             np.arange(Sq) + k.shape[1] - Sq, causal, window)
+        return o, lse
+    monkeypatch.setattr(oracle, "attention", attention_mod)
+    with pytest.raises(AssertionError):
+        test_gqa_equals_repeated_mha()
+
+
+# --- workload recipe sanity ---------------------------------------------------------------------
+def test_workload_recipe():
+    wl = WORKLOADS["decode_llama1b_b64"]
+    ctx = context_lens(wl)
+    assert ctx.min() >= 512 and ctx.max() <= 4096 and len(ctx) == 64
+    table, nb = paged_table(ctx, 16, wl.seed)
+    live = np.concatenate([table[b][: -(-int(c) // 16)] for b, c in enumerate(ctx)])
+    assert sorted(live.tolist()) == list(range(nb))
+
+
+def test_gather_mutants_are_caught(monkeypatch):
+    import oracle.attn_fp64 as oa
+
+    def swapped(pool, table_row, n_tokens, block_size):  # slot and block index exchanged
+        t = np.arange(n_tokens)
+        return pool[np.asarray(table_row)[t % block_size], :, t // block_size]
+    monkeypatch.setattr(oa, "gather_logical", swapped)
+    with pytest.raises((AssertionError, IndexError)):
+        test_brute_force_paged_decode(2, 0)
+
+
+def test_quantizer_rounding_mutant_is_caught(monkeypatch):
+    import oracle.attn_fp64 as oa
+    monkeypatch.setattr(oa.np, "rint", lambda x: np.floor(np.asarray(x) + 0.5))  # half away-ish
+    try:
+        with pytest.raises(AssertionError):
+            test_int8_hand_values()
+    finally:
+        monkeypatch.undo()
+
+
+def test_golden_regression():
+    """Oracle outputs on a small seeded case, written by tests/golden/make_golden.py."""
+    import json
+    import os
+    from tests.golden.make_golden import compute
+    path = os.path.join(os.path.dirname(__file__), "golden", "oracle_small.json")
+    with open(path) as f:
+        stored = json.load(f)
+    now = compute()
+    for key, val in stored.items():
+        assert np.abs(np.asarray(val) - np.asarray(now[key])).max() < 1e-12, key
