@@ -1,0 +1,117 @@
+// kv_cache_append: write new K/V rows into a paged cache, copying bf16 bits or quantizing to
+// INT8 with a per-(token, KV head) fp16 scale.
+//
+// Paged placement follows "分页KV缓存：借鉴操作系统的内存管理" on the Tiny-Infer page
+// ("从零构建CUDA推理引擎：Tiny-Infer项目的技术深度解析"): logical position -> (physical block
+// from the table, slot inside the block). INT8 storage follows "推测性解码与INT8量化" there;
+// the scale rule (absmax / 127, fp16, symmetric, ties-to-even) is this library's reading.
+//
+// HBM-bound elementwise work: one thread moves 8 elements (16 B of bf16 input); the D / 8
+// threads of one (token, head) row sit in adjacent lanes and reduce the row's absmax with
+// cross-lane shuffles. Division is IEEE (correctly rounded) so codes match a CPU reference
+// bit for bit.
+#include "common.h"
+#include "launch.h"
+#include <hip/hip_fp16.h>
+
+namespace attn {
+
+template <int D, bool I8>
+__global__ __launch_bounds__(256) void kv_append_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
+    const int32_t* __restrict__ table, void* __restrict__ k_cache, void* __restrict__ v_cache,
+    __half* __restrict__ k_scale, __half* __restrict__ v_scale, int64_t rows, int Hkv, int bs,
+    int num_seqs, int max_blocks, int num_blocks) {
+  constexpr int TPR = D / 8;  // threads per (token, head) row
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = gid / TPR;
+  const int c = (int)(gid % TPR);
+  const bool in_range = row < rows;
+  const int64_t r = in_range ? row : 0;
+  const int64_t t = r / Hkv;
+  const int g = (int)(r % Hkv);
+
+  bool valid = in_range;
+  int pb = 0, slot = 0;
+  if (valid) {
+    const int b = seq_idx[t];
+    const int p = pos[t];
+    valid = b >= 0 && b < num_seqs && p >= 0 && p < max_blocks * bs;
+    if (valid) {
+      pb = table[(int64_t)b * max_blocks + p / bs];
+      slot = p % bs;
+      valid = pb >= 0 && pb < num_blocks;
+    }
+  }
+  const int64_t src = r * D + c * 8;
+  const int64_t dst = pool_offset(pb, Hkv, g, bs, slot, D) + c * 8;
+
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const uint16_t* in = which == 0 ? k_new : v_new;
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (in_range) w = *reinterpret_cast<const u32x4*>(in + src);
+    if constexpr (!I8) {
+      uint16_t* out = reinterpret_cast<uint16_t*>(which == 0 ? k_cache : v_cache);
+      if (valid) *reinterpret_cast<u32x4*>(out + dst) = w;
+    } else {
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = bf16_lo(w[i]);
+        x[2 * i + 1] = bf16_hi(w[i]);
+      }
+      float a = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));
+#pragma unroll
+      for (int m = 1; m < TPR; m <<= 1) a = fmaxf(a, __shfl_xor(a, m, TPR));
+      const float s32 = __fdiv_rn(a, 127.0f);
+      const __half s16 = __float2half_rn(s32);
+      const float sf = __half2float(s16);
+      uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        int code = 0;
+        if (sf != 0.0f) {
+          float qv = rintf(__fdiv_rn(x[i], sf));
+          qv = fminf(fmaxf(qv, -127.0f), 127.0f);
+          code = (int)qv;
+        }
+        packed[i / 4] |= ((uint32_t)code & 0xffu) << (8 * (i % 4));
+      }
+      int8_t* out = reinterpret_cast<int8_t*>(which == 0 ? k_cache : v_cache);
+      __half* sc = which == 0 ? k_scale : v_scale;
+      if (valid) {
+        u32x2 pk = {packed[0], packed[1]};
+        *reinterpret_cast<u32x2*>(out + dst) = pk;
+        if (c == 0) sc[((int64_t)pb * Hkv + g) * bs + slot] = s16;
+      }
+    }
+  }
+}
+
+int launch_kv_append(const AppendArgs& a, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.T * a.Hkv;
+  const int tpr = a.D / 8;
+  const int64_t threads = rows * tpr;
+  const int block = 256;
+  const int64_t grid = (threads + block - 1) / block;
+  if (grid == 0) return 0;
+#define ATTN_APPEND(DD, I8)                                                                     \
+  hipLaunchKernelGGL((kv_append_kernel<DD, I8>), dim3((unsigned)grid), dim3(block), 0, stream, \
+                     (const uint16_t*)a.k_new, (const uint16_t*)a.v_new, a.seq_idx, a.pos,     \
+                     a.block_table, a.k_cache, a.v_cache, (__half*)a.k_scale,                  \
+                     (__half*)a.v_scale, rows, a.Hkv, a.block_size, a.num_seqs,                \
+                     a.max_blocks_per_seq, a.num_blocks)
+  if (a.D == 64) {
+    if (a.int8) ATTN_APPEND(64, true); else ATTN_APPEND(64, false);
+  } else {
+    if (a.int8) ATTN_APPEND(128, true); else ATTN_APPEND(128, false);
+  }
+#undef ATTN_APPEND
+  return 0;
+}
+
+}  // namespace attn

@@ -1,0 +1,157 @@
+// C ABI of libattn: host-side validation and dispatch. Every check runs before any HIP call,
+// so an invalid request returns a status code without touching the device.
+#include "../../include/attn.h"
+#include "launch.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return ATTN_OK;
+}
+
+int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool supported_d(int D) { return D == 64 || D == 128; }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_str(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "null pointer";
+    case ATTN_ERR_SHAPE: return "invalid shape or size";
+    case ATTN_ERR_DTYPE: return "invalid dtype";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int dtype,
+                 int B, int S, int Hq, int Hkv, int D, float scale, int causal, int window,
+                 void* stream) {
+  if (!q || !k || !v || !o) return fail(ATTN_ERR_NULL, "q, k, v and o are required");
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_DTYPE, "prefill dtype %d", dtype);
+  if (B < 1 || S < 1 || Hq < 1 || Hkv < 1) return fail(ATTN_ERR_SHAPE, "B, S, Hq, Hkv must be >= 1");
+  if (Hq % Hkv != 0) return fail(ATTN_ERR_SHAPE, "Hq %d is not a multiple of Hkv %d", Hq, Hkv);
+  if (window < 0) return fail(ATTN_ERR_SHAPE, "window %d < 0", window);
+  if (!(std::isfinite(scale) && scale > 0.f)) return fail(ATTN_ERR_SHAPE, "scale must be finite and > 0");
+  if (!supported_d(D)) return fail(ATTN_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+  if ((long long)B * S * Hq > (1LL << 31) / 2) return fail(ATTN_ERR_SHAPE, "B*S*Hq too large");
+  attn::PrefillArgs a{q, k, v, o, lse, B, S, Hq, Hkv, D, scale, causal != 0, window};
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == ATTN_BF16)
+    attn::launch_prefill_bf16(a, st);
+  else
+    attn::launch_prefill_f32(a, st);
+  return check_launch("attn_prefill");
+}
+
+size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_context_len, int window,
+                                  int split_tokens) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || max_context_len < 1 || window < 0 ||
+      split_tokens < 0)
+    return 0;
+  return attn::plan_decode(B, Hq, Hkv, D, max_context_len, window, split_tokens).workspace_bytes;
+}
+
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                      const void* k_scale, const void* v_scale, const int32_t* block_table,
+                      const int32_t* context_lens, void* o, int kv_dtype, int B, int Hq, int Hkv,
+                      int D, int block_size, int max_blocks_per_seq, int num_blocks,
+                      int max_context_len, float scale, int window, int split_tokens,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !context_lens || !o)
+    return fail(ATTN_ERR_NULL, "q, k_cache, v_cache, block_table, context_lens and o are required");
+  if (kv_dtype != ATTN_BF16 && kv_dtype != ATTN_I8)
+    return fail(ATTN_ERR_DTYPE, "decode kv_dtype %d", kv_dtype);
+  if (kv_dtype == ATTN_I8 && (!k_scale || !v_scale))
+    return fail(ATTN_ERR_NULL, "int8 cache needs k_scale and v_scale");
+  if (kv_dtype == ATTN_BF16 && (k_scale || v_scale))
+    return fail(ATTN_ERR_SHAPE, "k_scale/v_scale must be NULL for a bf16 cache");
+  if (B < 1 || Hq < 1 || Hkv < 1 || max_blocks_per_seq < 1 || num_blocks < 1 || max_context_len < 1)
+    return fail(ATTN_ERR_SHAPE, "B, Hq, Hkv, max_blocks_per_seq, num_blocks, max_context_len must be >= 1");
+  if (Hq % Hkv != 0) return fail(ATTN_ERR_SHAPE, "Hq %d is not a multiple of Hkv %d", Hq, Hkv);
+  if (window < 0) return fail(ATTN_ERR_SHAPE, "window %d < 0", window);
+  if (split_tokens < 0) return fail(ATTN_ERR_SHAPE, "split_tokens %d < 0", split_tokens);
+  if (!(std::isfinite(scale) && scale > 0.f)) return fail(ATTN_ERR_SHAPE, "scale must be finite and > 0");
+  if (!supported_d(D)) return fail(ATTN_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+  if (block_size != 16) return fail(ATTN_ERR_UNSUPPORTED, "block_size %d (supported: 16)", block_size);
+  if (Hq / Hkv > 16) return fail(ATTN_ERR_UNSUPPORTED, "Hq/Hkv = %d > 16", Hq / Hkv);
+  if (split_tokens % block_size != 0) return fail(ATTN_ERR_SHAPE, "split_tokens %d is not a multiple of block_size", split_tokens);
+  if (B > 65535 || Hkv > 65535) return fail(ATTN_ERR_SHAPE, "B and Hkv must be <= 65535");
+  attn::DecodePlan plan = attn::plan_decode(B, Hq, Hkv, D, max_context_len, window, split_tokens);
+  if (split_tokens != 0 && plan.split_tokens != split_tokens)
+    return fail(ATTN_ERR_UNSUPPORTED, "split_tokens %d exceeds the per-workgroup limit", split_tokens);
+  {
+    int gp = 1;
+    while (gp < Hq / Hkv) gp <<= 1;
+    if ((long long)gp * plan.split_tokens > 4096)
+      return fail(ATTN_ERR_UNSUPPORTED, "(Hq/Hkv rounded up to a power of two) * split_tokens must be <= 4096");
+  }
+  if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+    return fail(ATTN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", plan.workspace_bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  attn::DecodeArgs a{q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, o,
+                     kv_dtype == ATTN_I8, B, Hq, Hkv, D, block_size, max_blocks_per_seq,
+                     num_blocks, max_context_len, scale, window, plan, workspace};
+  attn::launch_decode(a, reinterpret_cast<hipStream_t>(stream));
+  return check_launch("attn_decode_paged");
+}
+
+int kv_cache_append(const void* k_new, const void* v_new, const int32_t* seq_idx,
+                    const int32_t* pos, const int32_t* block_table, void* k_cache, void* v_cache,
+                    void* k_scale, void* v_scale, int cache_dtype, int T, int Hkv, int D,
+                    int block_size, int num_seqs, int max_blocks_per_seq, int num_blocks,
+                    void* stream) {
+  if (cache_dtype != ATTN_BF16 && cache_dtype != ATTN_I8)
+    return fail(ATTN_ERR_DTYPE, "cache dtype %d", cache_dtype);
+  if (T < 0) return fail(ATTN_ERR_SHAPE, "T %d < 0", T);
+  if (Hkv < 1 || num_seqs < 1 || max_blocks_per_seq < 1 || num_blocks < 1)
+    return fail(ATTN_ERR_SHAPE, "Hkv, num_seqs, max_blocks_per_seq, num_blocks must be >= 1");
+  if (!supported_d(D)) return fail(ATTN_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+  if (block_size != 16) return fail(ATTN_ERR_UNSUPPORTED, "block_size %d (supported: 16)", block_size);
+  if ((long long)max_blocks_per_seq * block_size > 0x7fffffffLL)
+    return fail(ATTN_ERR_SHAPE, "max_blocks_per_seq * block_size overflows int32");
+  if (T == 0) return ok();
+  if (!k_new || !v_new || !seq_idx || !pos || !block_table || !k_cache || !v_cache)
+    return fail(ATTN_ERR_NULL, "k_new, v_new, seq_idx, pos, block_table, k_cache, v_cache are required");
+  if (cache_dtype == ATTN_I8 && (!k_scale || !v_scale))
+    return fail(ATTN_ERR_NULL, "int8 cache needs k_scale and v_scale");
+  attn::AppendArgs a{k_new, v_new, seq_idx, pos, block_table, k_cache, v_cache, k_scale, v_scale,
+                     cache_dtype == ATTN_I8, T, Hkv, D, block_size, num_seqs, max_blocks_per_seq,
+                     num_blocks};
+  attn::launch_kv_append(a, reinterpret_cast<hipStream_t>(stream));
+  return check_launch("kv_cache_append");
+}
+
+}  // extern "C"

@@ -1,0 +1,239 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass of the whole path on the Llama-3.2-1B-shaped workload:
+  1. kv_cache_append of the newest token of each of 64 sequences into the paged bf16 cache
+     (32 query heads, 8 KV heads, D = 64, block 16, contexts uniform in [512, 4096]),
+  2. a 512 MiB scratch write that evicts L2 and the Infinity Cache (so decode reads HBM),
+  3. attn_decode_paged over that cache (split-KV + log-sum-exp merge),
+  4. attn_prefill: causal GQA prefill, batch 1, S = 4096, 32/8 heads, D = 64, bf16.
+Each call is bracketed by HIP events on the stream the library launches on. The headline
+`value` is the prefill TFLOP/s (algorithmic flops: visible (query, key) pairs x 4D) over the
+timed steps; the decode HBM GB/s (algorithmic bytes: each visible K/V byte once, plus Q and O)
+is reported beside it. `--workload swa` / `int8_70b` time the other configurations the same way.
+
+Prints one JSON line. Inputs are seeded synthetic tensors (synth/) resident in HBM before the
+timed region starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_pairs(S: int, causal: bool, window: int) -> int:
+    """Visible (query, key) pairs of one head."""
+    if not causal:
+        return S * (S if window == 0 else min(S, window))  # not used by the workloads here
+    if window == 0 or window >= S:
+        return S * (S + 1) // 2
+    return window * (window + 1) // 2 + (S - window) * window
+
+
+def prefill_flops(wl) -> float:
+    return 4.0 * wl.D * wl.Hq * wl.B * prefill_pairs(wl.S, wl.causal, wl.window)
+
+
+def decode_bytes(wl, ctx) -> float:
+    vis = np.minimum(ctx, wl.window) if wl.window > 0 else ctx
+    per_tok = 2 * wl.Hkv * wl.D * (1 if wl.kv_dtype == "i8" else 2)
+    if wl.kv_dtype == "i8":
+        per_tok += 2 * wl.Hkv * 2  # fp16 scales of K and V
+    return float(vis.sum()) * per_tok + 2.0 * wl.B * wl.Hq * wl.D * 2
+
+
+def _bf16(t, bits):
+    return t.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(t.bfloat16).cuda()
+
+
+def setup_prefill(t, wl):
+    from synth import prefill_inputs
+    x = prefill_inputs(wl)
+    q, k, v = (_bf16(t, x[n + "_bits"]) for n in "qkv")
+    o = t.empty_like(q)
+    return dict(q=q, k=k, v=v, o=o)
+
+
+def setup_decode(t, wl):
+    """Paged cache, table, queries and the newest token's K/V for each sequence."""
+    import attention_attn_prefill_amd as A
+    from synth import context_lens, decode_query, new_tokens, paged_table, pool
+    ctx = context_lens(wl)
+    table, nb = paged_table(ctx, wl.block_size, wl.seed)
+    qbits, _ = decode_query(wl)
+    d = dict(ctx_np=ctx, table=t.from_numpy(table).cuda(), ctx=t.from_numpy(ctx).cuda(),
+             q=_bf16(t, qbits), nb=nb)
+    if wl.kv_dtype == "bf16":
+        d["kc"] = _bf16(t, pool(wl, "k", nb))
+        d["vc"] = _bf16(t, pool(wl, "v", nb))
+        d["ks"] = d["vs"] = None
+    else:  # quantize a bf16 pool in physical order with the library's append kernel
+        T = nb * wl.block_size
+        ident = t.arange(nb, dtype=t.int32, device="cuda")[None]
+        seq = t.zeros(T, dtype=t.int32, device="cuda")
+        pos = t.arange(T, dtype=t.int32, device="cuda")
+        for which in ("k", "v"):
+            src = pool(wl, which, nb)
+            rows = _bf16(t, np.ascontiguousarray(src.transpose(0, 2, 1, 3)).reshape(T, wl.Hkv, wl.D))
+            del src
+            c = t.empty((nb, wl.Hkv, wl.block_size, wl.D), dtype=t.int8, device="cuda")
+            s = t.empty((nb, wl.Hkv, wl.block_size), dtype=t.float16, device="cuda")
+            A.kv_cache_append(rows, rows, seq, pos, ident, c, c, k_scale=s, v_scale=s)
+            t.cuda.synchronize()
+            del rows
+            d[which + "c"], d[which + "s"] = c, s
+    kn, _ = new_tokens(wl.seed + 77, wl.B, wl.Hkv, wl.D, "k")
+    vn, _ = new_tokens(wl.seed + 78, wl.B, wl.Hkv, wl.D, "v")
+    d["kn"], d["vn"] = _bf16(t, kn), _bf16(t, vn)
+    d["seq"] = t.arange(wl.B, dtype=t.int32, device="cuda")
+    d["pos"] = (d["ctx"] - 1).to(t.int32)
+    d["o"] = t.empty_like(d["q"])
+    need = A.attn_decode_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.D, wl.ctx_hi, wl.window, 0)
+    d["ws"] = t.empty(max(need, 1), dtype=t.uint8, device="cuda")
+    return d
+
+
+def cpu_baseline(pwl, dwl, budget_s: float):
+    """The oracle, untuned, on a time-bounded sample of the same workload."""
+    import oracle
+    from synth import prefill_slab
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    G = pwl.Hq // pwl.Hkv
+    pos = np.arange(pwl.S)
+    heads, flops, t0 = 0, 0.0, time.perf_counter()
+    while heads < pwl.Hq * pwl.B and time.perf_counter() - t0 < budget_s:
+        b, h = divmod(heads, pwl.Hq)
+        q = prefill_slab(pwl, "q", b, h)
+        k = prefill_slab(pwl, "k", b, h // G)
+        v = prefill_slab(pwl, "v", b, h // G)
+        oracle.attention_head(q, k, v, pwl.scale, pos, pwl.causal, pwl.window)
+        heads += 1
+        flops += 4.0 * pwl.D * prefill_pairs(pwl.S, pwl.causal, pwl.window)
+    el = time.perf_counter() - t0
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 NumPy oracle prefill of {heads} of {pwl.Hq * pwl.B} (batch, head) pairs of "
+                      f"{pwl.name}, all {pwl.S} rows each, {el:.1f} s; BLAS threads = cores"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama1b", choices=["llama1b", "swa", "int8_70b"])
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0 = skip)")
+    ap.add_argument("--no-flush", action="store_true", help="skip the cache-evicting scratch write")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path is single-GPU; see the sharding notes in the design document)", file=sys.stderr)
+        return 2
+
+    import torch as t
+    import attention_attn_prefill_amd as A
+    from synth import WORKLOADS
+    A.lib()  # fail loudly if the HIP library is missing
+    assert t.cuda.is_available(), "bench.py needs a GPU"
+
+    pwl = {"llama1b": WORKLOADS["prefill_llama1b_s4096"], "swa": WORKLOADS["prefill_swa_s16384"],
+           "int8_70b": None}[args.workload]
+    dwl = {"llama1b": WORKLOADS["decode_llama1b_b64"], "swa": WORKLOADS["decode_swa_b32"],
+           "int8_70b": WORKLOADS["decode_int8_70b_b16"]}[args.workload]
+
+    P = setup_prefill(t, pwl) if pwl else None
+    Dd = setup_decode(t, dwl)
+    flush = t.empty(512 * 1024 * 1024 // 4, dtype=t.float32, device="cuda")
+    t.cuda.synchronize()
+
+    def step(ev=None):
+        e = ev or {}
+        if "a0" in e: e["a0"].record()
+        A.kv_cache_append(Dd["kn"], Dd["vn"], Dd["seq"], Dd["pos"], Dd["table"], Dd["kc"], Dd["vc"],
+                          k_scale=Dd["ks"], v_scale=Dd["vs"])
+        if "a1" in e: e["a1"].record()
+        if not args.no_flush:
+            flush.fill_(1.0)
+        if "d0" in e: e["d0"].record()
+        A.attn_decode_paged(Dd["q"], Dd["kc"], Dd["vc"], Dd["table"], Dd["ctx"], dwl.ctx_hi,
+                            k_scale=Dd["ks"], v_scale=Dd["vs"], scale=dwl.scale, window=dwl.window,
+                            out=Dd["o"], workspace=Dd["ws"])
+        if "d1" in e: e["d1"].record()
+        if P is not None:
+            if "p0" in e: e["p0"].record()
+            A.attn_prefill(P["q"], P["k"], P["v"], scale=pwl.scale, causal=pwl.causal, window=pwl.window,
+                           out=P["o"])
+            if "p1" in e: e["p1"].record()
+
+    for _ in range(args.warmup):
+        step()
+    t.cuda.synchronize()
+    evs = [{n: t.cuda.Event(enable_timing=True) for n in ("a0", "a1", "d0", "d1", "p0", "p1")}
+           for _ in range(args.steps)]
+    t.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    t.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+
+    def avg_ms(a, b):
+        return float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
+
+    d_ms = avg_ms("d0", "d1")
+    a_ms = avg_ms("a0", "a1")
+    dbytes = decode_bytes(dwl, Dd["ctx_np"])
+    d_gbs = dbytes / (d_ms * 1e-3) / 1e9
+    decode = {"kernel": "attn_decode_paged (split + merge)", "ms": d_ms, "GB/s": d_gbs,
+              "frac_hbm_peak": d_gbs / HBM_PEAK_GBS, "algorithmic_bytes": dbytes,
+              "tokens_per_s": dwl.B / (d_ms * 1e-3), "append_ms": a_ms,
+              "workload": f"{dwl.name}: B={dwl.B} Hq={dwl.Hq} Hkv={dwl.Hkv} D={dwl.D} kv={dwl.kv_dtype} "
+                          f"ctx=[{dwl.ctx_lo},{dwl.ctx_hi}] window={dwl.window} block=16"}
+    roofline_decode = {"bound": "hbm", "achieved": d_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": d_gbs / HBM_PEAK_GBS, "traffic": None}
+    out = {"metric": "paged decode attn HBM GB/s (% peak); prefill attn TFLOP/s (% MFMA peak)",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded N(0,1) tensors, bf16; no dataset)"}
+    if P is not None:
+        p_ms = avg_ms("p0", "p1")
+        pfl = prefill_flops(pwl)
+        p_tf = pfl / (p_ms * 1e-3) / 1e12
+        out.update(value=p_tf, unit="TFLOP/s")
+        out["roofline"] = {"bound": "mfma", "achieved": p_tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": p_tf / BF16_PEAK_TFLOPS, "traffic": None}
+        out["prefill"] = {"kernel": "attn_prefill (bf16 MFMA)", "ms": p_ms, "TFLOP/s": p_tf,
+                          "algorithmic_flops": pfl, "tokens_per_s": pwl.B * pwl.S / (p_ms * 1e-3),
+                          "workload": f"{pwl.name}: B={pwl.B} S={pwl.S} Hq={pwl.Hq} Hkv={pwl.Hkv} "
+                                      f"D={pwl.D} causal window={pwl.window}"}
+    else:
+        out.update(value=d_gbs, unit="GB/s")
+        out["roofline"] = roofline_decode
+    out["decode"] = decode
+    out["roofline_decode"] = roofline_decode
+    out["config"] = {"workload": (f"{pwl.name} + {dwl.name}" if pwl else dwl.name),
+                     "step": "kv_cache_append -> cache flush -> attn_decode_paged -> attn_prefill"}
+    if args.cpu_budget > 0 and pwl is not None:
+        out["cpu_baseline"] = cpu_baseline(pwl, dwl, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

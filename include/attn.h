@@ -1,0 +1,156 @@
+/*
+ * attn.h -- C ABI of libattn: fused prefill attention, paged-KV decode attention and KV-cache
+ * append for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (page title, section):
+ *  [TI] "从零构建CUDA推理引擎：Tiny-Infer项目的技术深度解析" (Tiny-Infer, a CUDA/C++ engine for
+ *       Llama 3.2 1B):
+ *       - "Flash Attention：内存与计算的重平衡": attention computed block by block with an online
+ *         softmax in on-chip memory, one thread block per (attention head, block of queries),
+ *         partial results accumulated on chip, the full score matrix never stored;
+ *       - "分页KV缓存：借鉴操作系统的内存管理": the KV cache is cut into fixed-size blocks and a
+ *         mapping table sends each logical position to a physical block;
+ *       - "推测性解码与INT8量化": the KV cache is stored in INT8 instead of FP16;
+ *       - "技术架构与模块设计": a static cache preallocated to the maximum context, with attention
+ *         changed to run incrementally (one new token against the cache) for decode.
+ *  [IL] "从零开始的LLM推理优化实验室：从PyTorch基线到Triton内核的完整实践",
+ *       "KV缓存实验与长上下文优化": static, growing and sliding-window caches.
+ *  [KD] "5 Fun Projects for LLM Inference Engineering" (KDnuggets), project 2 ("write your own
+ *       FlashAttention kernel in Triton"): tiling and the online softmax cut HBM<->on-chip traffic.
+ *
+ * Definition computed by every entry point (fp32 accumulation): for query row i of Sq rows
+ * against Lk keys, its position is P = Lk - Sq + i; key j is visible iff (not causal or
+ * j <= P) and (window == 0 or P - j < window); s_j = scale * q . k_j;
+ * o = sum_j softmax(s)_j v_j over the visible keys. Query head h reads KV head h / (Hq / Hkv).
+ *
+ * Conventions for every call:
+ *  - Every tensor argument is a device pointer owned by the caller; the library allocates no
+ *    memory and keeps no state beyond a thread-local last-error string.
+ *  - Every call only enqueues work on `stream` (a hipStream_t; NULL = the default stream) and
+ *    returns without synchronising. The result is ready when the stream reaches that point.
+ *  - Arguments are validated on the host before any launch; on a nonzero return nothing was
+ *    enqueued (except ATTN_ERR_HIP, returned when a launch itself fails).
+ *  - bf16 is IEEE bfloat16 stored as 16-bit words; fp16 is IEEE binary16; all tensors are dense,
+ *    row-major, with the last dimension contiguous.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  ATTN_ERR_DTYPE = 3,       /* unknown dtype code */
+  ATTN_ERR_UNSUPPORTED = 4, /* valid request that this build does not implement */
+  ATTN_ERR_WORKSPACE = 5,   /* workspace missing or smaller than attn_decode_workspace_size() */
+  ATTN_ERR_HIP = 6          /* a HIP launch failed; attn_last_error() holds the HIP message */
+};
+
+enum attn_dtype { ATTN_F32 = 0, ATTN_BF16 = 1, ATTN_I8 = 2 };
+
+/*
+ * attn_prefill -- tiled (FlashAttention-style) prefill attention with an online softmax.
+ * [TI] "Flash Attention：内存与计算的重平衡"; [KD] project 2; sliding window: [IL].
+ *
+ *  q, o : [B][S][Hq][D]  dtype (ATTN_F32 or ATTN_BF16); o gets the same dtype as q, rounded to
+ *                        nearest-even from fp32 for bf16.
+ *  k, v : [B][S][Hkv][D] same dtype.
+ *  lse  : optional fp32 [B][Hq][S], natural-log log-sum-exp of each row's scaled scores; NULL
+ *         to skip.
+ *  Sq = Lk = S, so query i sits at position i. causal != 0 applies the causal mask;
+ *  window = 0 means no window, window > 0 keeps the last `window` keys up to each query.
+ *  Requirements: B, S >= 1; Hkv >= 1; Hq a multiple of Hkv; D in {64, 128} (ATTN_ERR_UNSUPPORTED
+ *  otherwise); window >= 0; scale finite.
+ */
+int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int dtype, int B, int S, int Hq, int Hkv, int D,
+                 float scale, int causal, int window, void* stream);
+
+/*
+ * attn_decode_workspace_size -- bytes of device workspace attn_decode_paged needs for these
+ * sizes (0 when the call runs as a single pass and needs none). split_tokens as below.
+ */
+size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_context_len,
+                                  int window, int split_tokens);
+
+/*
+ * attn_decode_paged -- one new query token per sequence against a paged KV cache.
+ * [TI] "分页KV缓存：借鉴操作系统的内存管理" (block table), "技术架构与模块设计" (incremental
+ * decode against the cache), "推测性解码与INT8量化" (INT8 cache); sliding window: [IL].
+ *
+ *  q, o         : [B][Hq][D] bf16. Query b sits at position context_lens[b] - 1.
+ *  k_cache,
+ *  v_cache      : [num_blocks][Hkv][block_size][D], bf16 (kv_dtype ATTN_BF16) or int8
+ *                 (ATTN_I8). Logical token t of sequence b lives in slot t % block_size of
+ *                 physical block block_table[b][t / block_size].
+ *  k_scale,
+ *  v_scale      : fp16 [num_blocks][Hkv][block_size], required iff kv_dtype == ATTN_I8, else
+ *                 NULL. The value seen by attention is code * scale.
+ *  block_table  : int32 [B][max_blocks_per_seq]. Entries for blocks that hold no visible
+ *                 token (past the context, or wholly left of the window) are never read and
+ *                 may hold anything. A live entry outside [0, num_blocks) is not dereferenced:
+ *                 its tokens are skipped (the result is then meaningless, but no stray access
+ *                 happens).
+ *  context_lens : int32 [B], each in [1, min(max_context_len, max_blocks_per_seq*block_size)];
+ *                 values outside are clamped to that range on the device (0 or less gives o = 0).
+ *  max_context_len : host-side upper bound of context_lens, used to plan the split of the
+ *                 KV range across workgroups without reading device memory.
+ *  window       : 0 = no window; else only the last `window` positions are attended.
+ *  split_tokens : tokens per workgroup along the KV axis: 0 = the library's choice, else a
+ *                 positive multiple of block_size. Partials are merged by log-sum-exp.
+ *  workspace    : device buffer of at least attn_decode_workspace_size(...) bytes (may be NULL
+ *                 when that size is 0); overwritten by the call; its contents on entry do not
+ *                 matter. Two calls in flight at once must not share a workspace.
+ *  Requirements: D in {64, 128}; block_size == 16; Hq % Hkv == 0 and Hq / Hkv <= 16.
+ */
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                      const void* k_scale, const void* v_scale,
+                      const int32_t* block_table, const int32_t* context_lens, void* o,
+                      int kv_dtype, int B, int Hq, int Hkv, int D,
+                      int block_size, int max_blocks_per_seq, int num_blocks,
+                      int max_context_len, float scale, int window, int split_tokens,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kv_cache_append -- write T new K/V rows into the paged cache.
+ * [TI] "技术架构与模块设计" (cache written as tokens are produced), "分页KV缓存：借鉴操作系统的内存管理"
+ * (logical position -> physical block through the table), "推测性解码与INT8量化" (INT8 storage).
+ *
+ *  k_new, v_new : [T][Hkv][D] bf16.
+ *  seq_idx, pos : int32 [T]; row t goes to sequence seq_idx[t] at logical position pos[t], i.e.
+ *                 slot pos % block_size of block block_table[seq_idx][pos / block_size].
+ *  block_table  : int32 [num_seqs][max_blocks_per_seq].
+ *  k_cache, v_cache, k_scale, v_scale : as in attn_decode_paged. cache_dtype ATTN_BF16 copies
+ *                 the bits; ATTN_I8 quantizes each (token, KV head) row of D values:
+ *                 a = max|x|, scale = fp16(fp32(a) / 127) (IEEE division, round to nearest
+ *                 even), code = clamp(rint(x / fp32(scale)), -127, 127) with ties to even; a
+ *                 zero scale gives zero codes.
+ *  Rows whose seq_idx is outside [0, num_seqs), whose pos is outside
+ *  [0, max_blocks_per_seq*block_size), or whose table entry is outside [0, num_blocks) are not
+ *  written. Two rows aimed at the same slot leave one of them, unspecified which.
+ *  Requirements: T >= 0 (T == 0 is a no-op); D in {64, 128}; block_size == 16.
+ */
+int kv_cache_append(const void* k_new, const void* v_new, const int32_t* seq_idx,
+                    const int32_t* pos, const int32_t* block_table,
+                    void* k_cache, void* v_cache, void* k_scale, void* v_scale,
+                    int cache_dtype, int T, int Hkv, int D, int block_size,
+                    int num_seqs, int max_blocks_per_seq, int num_blocks, void* stream);
+
+/* Static string naming a status code. */
+const char* attn_status_str(int status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -96,8 +96,9 @@ def _rng(*key: int) -> np.random.Generator:
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round finite fp32 values to bf16 (nearest, ties to even); returns the uint16 bit patterns."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    # finite inputs: the largest sum, 0xFF7FFFFF + 0x8000, still fits in 32 bits
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return rounded.astype(np.uint16)
 
 

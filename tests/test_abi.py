@@ -1,0 +1,118 @@
+"""CPU checks of the C ABI: the library loads, exports every function include/attn.h declares,
+and rejects invalid arguments with the documented status codes before touching a device.
+
+No call here reaches a kernel launch: every argument set below fails host-side validation.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_attn_prefill_amd as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("attn_prefill", "attn_decode_paged", "kv_cache_append", "attn_decode_workspace_size",
+              "attn_status_str", "attn_last_error"):
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol():
+    L = A.lib()
+    for n in _declared():
+        assert hasattr(L, n), f"libattn.so does not export {n}"
+    assert set(_declared()) == set(A._SIGS), "binding signatures out of sync with the header"
+
+
+def test_status_strings():
+    L = A.lib()
+    assert L.attn_status_str(0) == b"ok"
+    assert L.attn_status_str(A.ATTN_ERR_WORKSPACE).startswith(b"workspace")
+    assert L.attn_status_str(99) == b"unknown status"
+
+
+def _prefill(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, dtype=A.ATTN_BF16, B=1, S=8, Hq=4, Hkv=2,
+                D=64, scale=0.125, causal=1, window=0)
+    args.update(kw)
+    return A.lib().attn_prefill(args["q"], args["k"], args["v"], args["o"], args["lse"], args["dtype"],
+                                args["B"], args["S"], args["Hq"], args["Hkv"], args["D"], args["scale"],
+                                args["causal"], args["window"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), A.ATTN_ERR_NULL), (dict(o=None), A.ATTN_ERR_NULL),
+    (dict(dtype=A.ATTN_I8), A.ATTN_ERR_DTYPE), (dict(dtype=7), A.ATTN_ERR_DTYPE),
+    (dict(B=0), A.ATTN_ERR_SHAPE), (dict(S=0), A.ATTN_ERR_SHAPE), (dict(Hq=3), A.ATTN_ERR_SHAPE),
+    (dict(window=-1), A.ATTN_ERR_SHAPE), (dict(scale=0.0), A.ATTN_ERR_SHAPE),
+    (dict(scale=float("nan")), A.ATTN_ERR_SHAPE), (dict(D=96), A.ATTN_ERR_UNSUPPORTED),
+    (dict(D=256), A.ATTN_ERR_UNSUPPORTED),
+])
+def test_prefill_validation(kw, code):
+    assert _prefill(**kw) == code
+    assert A.lib().attn_last_error() != b""
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, ks=None, vs=None, table=FAKE, ctx=FAKE, o=FAKE,
+             kv=A.ATTN_BF16, B=2, Hq=8, Hkv=2, D=64, bs=16, mb=4, nb=8, maxctx=64, scale=0.125,
+             window=0, split=0, ws=None, wsb=0)
+    a.update(kw)
+    return A.lib().attn_decode_paged(a["q"], a["kc"], a["vc"], a["ks"], a["vs"], a["table"], a["ctx"],
+                                     a["o"], a["kv"], a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["mb"],
+                                     a["nb"], a["maxctx"], a["scale"], a["window"], a["split"], a["ws"],
+                                     a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), A.ATTN_ERR_NULL), (dict(table=None), A.ATTN_ERR_NULL), (dict(ctx=None), A.ATTN_ERR_NULL),
+    (dict(kv=A.ATTN_F32), A.ATTN_ERR_DTYPE), (dict(kv=A.ATTN_I8), A.ATTN_ERR_NULL),
+    (dict(ks=FAKE, vs=FAKE), A.ATTN_ERR_SHAPE), (dict(Hq=6, Hkv=4), A.ATTN_ERR_SHAPE),
+    (dict(maxctx=0), A.ATTN_ERR_SHAPE), (dict(window=-2), A.ATTN_ERR_SHAPE), (dict(split=-16), A.ATTN_ERR_SHAPE),
+    (dict(split=24), A.ATTN_ERR_SHAPE), (dict(D=80), A.ATTN_ERR_UNSUPPORTED), (dict(bs=8), A.ATTN_ERR_UNSUPPORTED),
+    (dict(Hq=34, Hkv=2), A.ATTN_ERR_UNSUPPORTED), (dict(split=4096), A.ATTN_ERR_UNSUPPORTED),
+    (dict(maxctx=5000, split=64), A.ATTN_ERR_WORKSPACE),
+    (dict(maxctx=5000, split=64, ws=FAKE, wsb=16), A.ATTN_ERR_WORKSPACE),
+])
+def test_decode_validation(kw, code):
+    assert _decode(**kw) == code
+
+
+def test_workspace_size_rules():
+    ws = A.attn_decode_workspace_size
+    assert ws(2, 8, 2, 64, 64, 0, 64) == 0  # one split: no workspace
+    n = ws(2, 8, 2, 64, 5000, 0, 64)        # 79 splits
+    assert n >= 2 * 8 * 79 * (64 + 1) * 4
+    assert ws(2, 8, 2, 64, 5000, 100, 64) < n  # the window bounds the splits
+    assert ws(0, 8, 2, 64, 64, 0, 0) == 0
+
+
+def _append(**kw):
+    a = dict(kn=FAKE, vn=FAKE, seq=FAKE, pos=FAKE, table=FAKE, kc=FAKE, vc=FAKE, ks=None, vs=None,
+             dt=A.ATTN_BF16, T=4, Hkv=2, D=64, bs=16, ns=2, mb=4, nb=8)
+    a.update(kw)
+    return A.lib().kv_cache_append(a["kn"], a["vn"], a["seq"], a["pos"], a["table"], a["kc"], a["vc"],
+                                   a["ks"], a["vs"], a["dt"], a["T"], a["Hkv"], a["D"], a["bs"],
+                                   a["ns"], a["mb"], a["nb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kn=None), A.ATTN_ERR_NULL), (dict(kc=None), A.ATTN_ERR_NULL),
+    (dict(dt=A.ATTN_I8), A.ATTN_ERR_NULL), (dict(dt=A.ATTN_F32), A.ATTN_ERR_DTYPE),
+    (dict(T=-1), A.ATTN_ERR_SHAPE), (dict(Hkv=0), A.ATTN_ERR_SHAPE), (dict(D=32), A.ATTN_ERR_UNSUPPORTED),
+    (dict(bs=32), A.ATTN_ERR_UNSUPPORTED), (dict(T=0, kn=None), A.ATTN_OK),
+])
+def test_append_validation(kw, code):
+    assert _append(**kw) == code
