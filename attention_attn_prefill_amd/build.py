@@ -13,6 +13,7 @@ SOURCES = ["attn_api.cpp", "append.hip", "decode.hip", "prefill_bf16.hip", "pref
 
 # Packed-fp32 VALU forms are kept out of the code objects on purpose.
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function"]
 

@@ -108,16 +108,10 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
   if (block_size != 16) return fail(ATTN_ERR_UNSUPPORTED, "block_size %d (supported: 16)", block_size);
   if (Hq / Hkv > 16) return fail(ATTN_ERR_UNSUPPORTED, "Hq/Hkv = %d > 16", Hq / Hkv);
   if (split_tokens % block_size != 0) return fail(ATTN_ERR_SHAPE, "split_tokens %d is not a multiple of block_size", split_tokens);
+  if (split_tokens > attn::kMaxSplitTokens)
+    return fail(ATTN_ERR_UNSUPPORTED, "split_tokens %d > %d", split_tokens, attn::kMaxSplitTokens);
   if (B > 65535 || Hkv > 65535) return fail(ATTN_ERR_SHAPE, "B and Hkv must be <= 65535");
   attn::DecodePlan plan = attn::plan_decode(B, Hq, Hkv, D, max_context_len, window, split_tokens);
-  if (split_tokens != 0 && plan.split_tokens != split_tokens)
-    return fail(ATTN_ERR_UNSUPPORTED, "split_tokens %d exceeds the per-workgroup limit", split_tokens);
-  {
-    int gp = 1;
-    while (gp < Hq / Hkv) gp <<= 1;
-    if ((long long)gp * plan.split_tokens > 4096)
-      return fail(ATTN_ERR_UNSUPPORTED, "(Hq/Hkv rounded up to a power of two) * split_tokens must be <= 4096");
-  }
   if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
     return fail(ATTN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", plan.workspace_bytes,
                 workspace ? workspace_bytes : (size_t)0);

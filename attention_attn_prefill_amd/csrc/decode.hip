@@ -12,13 +12,19 @@
 // Design (gfx950): one workgroup of 4 waves per (split, KV head g, sequence b). A split is a
 // run of `C` consecutive logical tokens, block aligned. All G = Hq/Hkv query heads of g are
 // served by the same workgroup, so every K/V byte is read from HBM once.
-//   pass 1  QK^T on MFMA 16x16x32: A = 16 tokens of a K block (natural [token][d] rows),
-//           B = Q^T of the G heads (padded to 16 columns). Scores (log2 units) go to LDS.
-//   pass 2  per-head max and exp2 over the split's scores in LDS; row sums.
-//   pass 3  PV on the VALU: each lane owns 8 consecutive d of one token, multiplies by the G
-//           probabilities and accumulates; lanes are then reduced.
-//   final   o = acc / l  (single split: bf16 output directly)  or a partial (o, lse) in fp32
-//           workspace, merged by decode_merge_kernel.
+// Each wave walks the split in chunks of U blocks; for a chunk it
+//   * issues the table lookups and every K and V load of the chunk at once (deep memory-level
+//     parallelism: 16-32 KB in flight per wave),
+//   * computes QK^T on MFMA 16x16x32: A = 16 tokens of a K block in their natural [token][d]
+//     rows, B = Q^T of the G heads (padded to 16 columns); for INT8 the codes are widened to
+//     fp16 (exact) and the per-token scale is applied to the fp32 score,
+//   * runs the online softmax per head in the log2 domain, moving the running max (and
+//     rescaling the accumulators) only when it grows by more than 8,
+//   * hands the probabilities to the PV lanes through a small per-wave LDS slice and does PV on
+//     the VALU, each lane owning 8 consecutive d of one token (coalesced V rows); the INT8 V
+//     scale is folded into the probability.
+// The 4 waves' (m, l, acc) are merged by log-sum-exp in LDS; the workgroup then writes the
+// bf16 output (single split) or an fp32 partial (o, lse) merged by decode_merge_kernel.
 #include "common.h"
 #include "launch.h"
 #include <hip/hip_fp16.h>
@@ -29,7 +35,7 @@ namespace attn {
 
 constexpr int kDecodeThreads = 256;
 constexpr int kDecodeWaves = 4;
-constexpr int kScoreFloats = 4096;  // LDS score buffer: G * split_tokens <= 4096
+constexpr int kMaxSplitBlocks = kMaxSplitTokens / 16;  // the table slice is kept in LDS
 
 __device__ __forceinline__ int decode_ctx(const int32_t* ctx_lens, int b, int max_ctx,
                                           int max_blocks, int bs) {
@@ -37,6 +43,30 @@ __device__ __forceinline__ int decode_ctx(const int32_t* ctx_lens, int b, int ma
   int cap = min(max_ctx, max_blocks * bs);
   return c < 0 ? 0 : (c > cap ? cap : c);
 }
+
+// xor-16 / xor-32 lane partners within a wave
+__device__ __forceinline__ float max_x32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_x32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Chunks of U blocks (U*16 tokens) are the unit of work of one wave: their K and V loads are
+// all issued before any of them is consumed.
+template <int D, bool I8>
+struct DecodeShape {
+  static constexpr int BS = 16;
+  static constexpr int U = (D == 64 || I8) ? 4 : 2;       // blocks per chunk
+  static constexpr int KSTEPS = D / 32;                    // MFMA k-steps per block
+  static constexpr int KLOADS = I8 ? D / 64 : D / 32;      // 16-byte K loads per lane per block
+  static constexpr int VBYTES = I8 ? 8 : 16;               // bytes per lane per V load (8 elements)
+  static constexpr int CPR = D / 8;                        // lanes per V row
+  static constexpr int TPW = 64 / CPR;                     // tokens per V load instruction
+  static constexpr int VLOADS = BS / TPW;                  // V loads per lane per block
+};
 
 template <int D, int GP, bool I8>
 __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
@@ -47,20 +77,23 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     float* __restrict__ part_o, float* __restrict__ part_lse, int Hq, int Hkv, int G,
     int max_blocks, int num_blocks, int max_ctx, float scale_log2, int window, int C,
     int n_split) {
-  constexpr int BS = 16;
-  __shared__ float s_scores[kScoreFloats];
+  using SH = DecodeShape<D, I8>;
+  constexpr int BS = SH::BS, U = SH::U, CT = U * BS;  // CT tokens per chunk
+  __shared__ float s_p[kDecodeWaves][CT][GP];       // probabilities handed to the PV lanes
+  __shared__ float s_alpha[kDecodeWaves][GP];
   __shared__ float s_red[kDecodeWaves][GP][D];
-  __shared__ float s_m[GP], s_l[GP];
+  __shared__ float s_ml[kDecodeWaves][2][GP];
+  __shared__ int s_pb[kMaxSplitBlocks];  // the split's slice of the block table
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   const int ctx = decode_ctx(ctx_lens, b, max_ctx, max_blocks, BS);
   const int lo = window > 0 ? max(0, ctx - window) : 0;
   const int base = lo & ~(BS - 1);
   const int t_begin = base + split * C;
   if (ctx <= 0) {
-    // Empty context: the output is defined as zero. Split 0 writes it (merge sees n_valid=0).
     if (split == 0 && n_split == 1) {
       for (int i = threadIdx.x; i < G * D; i += kDecodeThreads)
         out[((int64_t)b * Hq + g * G) * D + i] = 0;
@@ -71,20 +104,28 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
   const int t_end = min(t_begin + C, ctx);
   const int nblk = (t_end - t_begin + BS - 1) / BS;
   const int lb0 = t_begin / BS;
-  const int32_t* trow = table + (int64_t)b * max_blocks;
-
-  // ---- pass 1: scores on MFMA -------------------------------------------------------------
-  const int hq = lane & 15;    // MFMA column = query head within the group
-  const int grp = lane >> 4;   // 0..3
   {
-    constexpr int KSTEPS = D / 32;
-    typedef typename std::conditional<I8, f16x8, bf16x8>::type frag_t;
-    frag_t qf[KSTEPS];
+    const int32_t* trow = table + (int64_t)b * max_blocks + lb0;
+    for (int i = threadIdx.x; i < nblk; i += kDecodeThreads) {
+      const int e = trow[i];
+      s_pb[i] = (e >= 0 && e < num_blocks) ? e : -1;  // -1: entry unusable, tokens skipped
+    }
+  }
+  __syncthreads();
+
+  // MFMA (QK^T) lane roles: column = query head, rows = 4 tokens of the block
+  const int hq = lane & 15, grp = lane >> 4;
+  // PV lane roles: 8 consecutive d of one token
+  const int c8 = lane % SH::CPR, ts = lane / SH::CPR;
+
+  typedef typename std::conditional<I8, f16x8, bf16x8>::type frag_t;
+  frag_t qf[SH::KSTEPS];
+  {
     const uint16_t* qrow = q + ((int64_t)b * Hq + g * G + hq) * D;
 #pragma unroll
-    for (int j = 0; j < KSTEPS; ++j) {
-      // k-step j covers d = 32j + 8*grp + e for bf16; for int8, the d set of step j is
-      // 64*(j/2) + 16*grp + 8*(j%2) + e (one 16-byte load feeds two steps).
+    for (int j = 0; j < SH::KSTEPS; ++j) {
+      // bf16: step j covers d = 32j + 8*grp + e; int8: one 16-byte load feeds steps 2jj, 2jj+1
+      // covering d = 64*jj + 16*grp + 8*sub + e.
       const int d0 = I8 ? (64 * (j / 2) + 16 * grp + 8 * (j % 2)) : (32 * j + 8 * grp);
       u32x4 w = {0u, 0u, 0u, 0u};
       if (hq < G) w = *reinterpret_cast<const u32x4*>(qrow + d0);
@@ -98,153 +139,208 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
         qf[j] = __builtin_bit_cast(bf16x8, w);
       }
     }
-
-    for (int blk = wave; blk < nblk; blk += kDecodeWaves) {
-      const int pb = trow[lb0 + blk];
-      const bool ok = pb >= 0 && pb < num_blocks;
-      const int tok = 4 * grp;  // first of this lane's 4 accumulator rows
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      float ksc[4] = {1.f, 1.f, 1.f, 1.f};
-      if (ok) {
-        const int64_t row = pool_offset(pb, Hkv, g, BS, lane & 15, D);
-        if constexpr (I8) {
-          const int8_t* kc = reinterpret_cast<const int8_t*>(k_cache) + row;
-#pragma unroll
-          for (int jj = 0; jj < D / 64; ++jj) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(kc + 64 * jj + 16 * grp);
-#pragma unroll
-            for (int sub = 0; sub < 2; ++sub) {
-              f16x8 a;
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const uint32_t word = w[2 * sub + e / 4];
-                a[e] = (_Float16)(int)(int8_t)(word >> (8 * (e % 4)));
-              }
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[2 * jj + sub], acc, 0, 0, 0);
-            }
-          }
-          const __half* ks = k_scale + ((int64_t)pb * Hkv + g) * BS + tok;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) ksc[i] = __half2float(ks[i]);
-        } else {
-          const uint16_t* kc = reinterpret_cast<const uint16_t*>(k_cache) + row;
-#pragma unroll
-          for (int j = 0; j < KSTEPS; ++j) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(kc + 32 * j + 8 * grp);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), qf[j],
-                                                          acc, 0, 0, 0);
-          }
-        }
-      }
-      if (hq < G) {
-        f32x4 s;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = t_begin + blk * BS + tok + i;
-          const bool vis = ok && t >= lo && t < t_end;
-          s[i] = vis ? acc[i] * ksc[i] * scale_log2 : -INFINITY;
-        }
-        *reinterpret_cast<f32x4*>(&s_scores[hq * C + blk * BS + tok]) = s;
-      }
-    }
   }
-  __syncthreads();
 
-  // ---- pass 2: per-head max, probabilities, sums -----------------------------------------
-  const int ntok = nblk * BS;
-  for (int h = wave; h < G; h += kDecodeWaves) {
-    float m = kNegBig;
-    for (int i = lane; i < ntok; i += 64) m = fmaxf(m, s_scores[h * C + i]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    float l = 0.f;
-    for (int i = lane; i < ntok; i += 64) {
-      const float p = fast_exp2(s_scores[h * C + i] - m);
-      s_scores[h * C + i] = p;
-      l += p;
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
-    if (lane == 0) {
-      s_m[h] = m;
-      s_l[h] = l;
-    }
-  }
-  __syncthreads();
-
-  // ---- pass 3: PV on the VALU ------------------------------------------------------------
-  constexpr int CPR = D / 8;      // lanes per token row (8 elements each)
-  constexpr int TPW = 64 / CPR;   // tokens per wave step
-  const int c = lane % CPR, ts = lane / CPR;
+  float m_run = kNegBig;  // per head (lanes hq), log2 units
+  float l_part = 0.f;     // this lane's share of the row sum
   float acc[GP][8];
 #pragma unroll
   for (int h = 0; h < GP; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
 
-  for (int blk = wave; blk < nblk; blk += kDecodeWaves) {
-    const int pb = trow[lb0 + blk];
-    if (!(pb >= 0 && pb < num_blocks)) continue;
+  const int nchunk = (nblk + U - 1) / U;
+  for (int ch = wave; ch < nchunk; ch += kDecodeWaves) {
+    const int blk0 = ch * U;
+    int pb[U];
+    bool okb[U];
 #pragma unroll
-    for (int tt = 0; tt < BS; tt += TPW) {
-      const int slot = tt + ts;
-      const int tpos = t_begin + blk * BS + slot;
-      if (tpos < lo || tpos >= t_end) continue;  // masked slot: may hold anything (even NaN)
-      const int64_t off = pool_offset(pb, Hkv, g, BS, slot, D) + 8 * c;
-      float x[8];
-      float vsc = 1.f;
+    for (int u = 0; u < U; ++u) {
+      const int blk = blk0 + u;
+      pb[u] = __builtin_amdgcn_readfirstlane(blk < nblk ? s_pb[blk] : -1);
+      okb[u] = pb[u] >= 0;
+      if (!okb[u]) pb[u] = 0;
+    }
+    // ---- issue every load of the chunk -------------------------------------------------
+    u32x4 kw[U][SH::KLOADS];
+    typedef typename std::conditional<I8, u32x2, u32x4>::type vword_t;
+    vword_t vw[U][SH::VLOADS];
+    float ksc[U][4], vsc[U][SH::VLOADS];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t brow = pool_offset(pb[u], Hkv, g, BS, 0, D);
       if constexpr (I8) {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(
-            reinterpret_cast<const int8_t*>(v_cache) + off);
+        const int8_t* kc = reinterpret_cast<const int8_t*>(k_cache) + brow + (int64_t)hq * D;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = (float)(int8_t)(w[e / 4] >> (8 * (e % 4)));
-        vsc = __half2float(v_scale[((int64_t)pb * Hkv + g) * BS + slot]);
+        for (int jj = 0; jj < SH::KLOADS; ++jj)
+          kw[u][jj] = *reinterpret_cast<const u32x4*>(kc + 64 * jj + 16 * grp);
+        const int8_t* vc = reinterpret_cast<const int8_t*>(v_cache) + brow;
+#pragma unroll
+        for (int i = 0; i < SH::VLOADS; ++i)
+          vw[u][i] = *reinterpret_cast<const u32x2*>(vc + (int64_t)(i * SH::TPW + ts) * D + 8 * c8);
+        const __half* ks = k_scale + ((int64_t)pb[u] * Hkv + g) * BS;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ksc[u][i] = __half2float(ks[4 * grp + i]);
+        const __half* vs = v_scale + ((int64_t)pb[u] * Hkv + g) * BS;
+#pragma unroll
+        for (int i = 0; i < SH::VLOADS; ++i) vsc[u][i] = __half2float(vs[i * SH::TPW + ts]);
       } else {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(
-            reinterpret_cast<const uint16_t*>(v_cache) + off);
+        const uint16_t* kc = reinterpret_cast<const uint16_t*>(k_cache) + brow + (int64_t)hq * D;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[2 * e] = bf16_lo(w[e]);
-          x[2 * e + 1] = bf16_hi(w[e]);
-        }
+        for (int j = 0; j < SH::KLOADS; ++j)
+          kw[u][j] = *reinterpret_cast<const u32x4*>(kc + 32 * j + 8 * grp);
+        const uint16_t* vc = reinterpret_cast<const uint16_t*>(v_cache) + brow;
+#pragma unroll
+        for (int i = 0; i < SH::VLOADS; ++i)
+          vw[u][i] = *reinterpret_cast<const u32x4*>(vc + (int64_t)(i * SH::TPW + ts) * D + 8 * c8);
       }
-      const int li = blk * BS + slot;
+    }
+    // ---- scores on MFMA ---------------------------------------------------------------
+    float sc[U][4];
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (I8) {
+#pragma unroll
+        for (int jj = 0; jj < SH::KLOADS; ++jj)
+#pragma unroll
+          for (int sub = 0; sub < 2; ++sub) {
+            f16x8 a;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t word = kw[u][jj][2 * sub + e / 4];
+              a[e] = (_Float16)(int)(int8_t)(word >> (8 * (e % 4)));
+            }
+            a4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[2 * jj + sub], a4, 0, 0, 0);
+          }
+      } else {
+#pragma unroll
+        for (int j = 0; j < SH::KSTEPS; ++j)
+          a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw[u][j]), qf[j], a4, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t_begin + (blk0 + u) * BS + 4 * grp + i;
+        const bool vis = okb[u] && t >= lo && t < t_end;
+        float s = a4[i] * scale_log2;
+        if constexpr (I8) s *= ksc[u][i];
+        sc[u][i] = vis ? s : -INFINITY;
+        cmax = fmaxf(cmax, sc[u][i]);
+      }
+    }
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+    cmax = max_x32(cmax);
+    // lazy rescale: move the running max only when it grows by more than 8 (log2 units)
+    if (__builtin_amdgcn_ballot_w64(cmax > m_run + 8.0f) != 0) {
+      const float m_new = fmaxf(m_run, cmax);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_part *= alpha;
+      if (grp == 0 && hq < GP) s_alpha[wave][hq] = alpha;
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int h = 0; h < GP; ++h) {
-        if (h < G) {
-          const float p = s_scores[h * C + li] * vsc;
+        const float al = s_alpha[wave][h];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= al;
+      }
+    }
+    // probabilities -> LDS [token][head]
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = fast_exp2(sc[u][i] - m_run);
+        l_part += p;
+        if (hq < GP) s_p[wave][u * BS + 4 * grp + i][hq] = p;
+      }
+    __builtin_amdgcn_wave_barrier();
+    // ---- PV on the VALU -----------------------------------------------------------------
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < SH::VLOADS; ++i) {
+        const int slot = i * SH::TPW + ts;
+        const int tpos = t_begin + (blk0 + u) * BS + slot;
+        if (!(okb[u] && tpos >= lo && tpos < t_end)) continue;  // masked slot may hold NaN
+        float x[8];
+        if constexpr (I8) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = (float)(int8_t)(vw[u][i][e / 4] >> (8 * (e % 4)));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[2 * e] = bf16_lo(vw[u][i][e]);
+            x[2 * e + 1] = bf16_hi(vw[u][i][e]);
+          }
+        }
+        float pv[GP];
+#pragma unroll
+        for (int h4 = 0; h4 < GP; h4 += 4) {
+          if constexpr (GP >= 4) {
+            const f32x4 p4 = *reinterpret_cast<const f32x4*>(&s_p[wave][u * BS + slot][h4]);
+            pv[h4] = p4[0]; pv[h4 + 1] = p4[1]; pv[h4 + 2] = p4[2]; pv[h4 + 3] = p4[3];
+          } else {
+#pragma unroll
+            for (int h = 0; h < GP; ++h) pv[h] = s_p[wave][u * BS + slot][h];
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < GP; ++h) {
+          float p = pv[h];
+          if constexpr (I8) p *= vsc[u][i];
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, x[e], acc[h][e]);
         }
       }
-    }
+    __builtin_amdgcn_wave_barrier();  // s_p is rewritten by the next chunk
   }
-  // reduce over the token slots of the wave (lanes with equal c)
+
+  // ---- reduce inside the wave ------------------------------------------------------------
+  // row sum: lanes hq, hq+16, hq+32, hq+48
+  float l_w = l_part + __shfl_xor(l_part, 16);
+  l_w = sum_x32(l_w);
+  // PV accumulators: lanes with equal c8
 #pragma unroll
   for (int h = 0; h < GP; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll
-      for (int o = CPR; o < 64; o <<= 1) acc[h][e] += __shfl_xor(acc[h][e], o);
+      for (int o = SH::CPR; o < 64; o <<= 1) acc[h][e] += __shfl_xor(acc[h][e], o);
   if (ts == 0) {
 #pragma unroll
     for (int h = 0; h < GP; ++h)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s_red[wave][h][8 * c + e] = acc[h][e];
+      for (int e = 0; e < 8; ++e) s_red[wave][h][8 * c8 + e] = acc[h][e];
+  }
+  if (grp == 0 && hq < GP) {
+    s_ml[wave][0][hq] = m_run;
+    s_ml[wave][1][hq] = l_w;
   }
   __syncthreads();
 
+  // ---- merge the 4 waves and write ---------------------------------------------------------
   for (int i = threadIdx.x; i < G * D; i += kDecodeThreads) {
     const int h = i / D, d = i % D;
-    const float sum = s_red[0][h][d] + s_red[1][h][d] + s_red[2][h][d] + s_red[3][h][d];
-    const float inv = 1.0f / s_l[h];
+    float M = s_ml[0][0][h];
+#pragma unroll
+    for (int w = 1; w < kDecodeWaves; ++w) M = fmaxf(M, s_ml[w][0][h]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) {
+      const float wt = fast_exp2(s_ml[w][0][h] - M);  // waves that saw no token: l = 0, acc = 0
+      num = fmaf(wt, s_red[w][h][d], num);
+      den = fmaf(wt, s_ml[w][1][h], den);
+    }
+    const float inv = 1.0f / den;
     const int head = g * G + h;
     if (n_split == 1) {
-      out[((int64_t)b * Hq + head) * D + d] = (uint16_t)f32_to_bf16_bits(sum * inv);
+      out[((int64_t)b * Hq + head) * D + d] = (uint16_t)f32_to_bf16_bits(num * inv);
     } else {
       const int64_t pi = ((int64_t)b * Hq + head) * n_split + split;
-      part_o[pi * D + d] = sum * inv;
-      if (d == 0) part_lse[pi] = s_m[h] + __log2f(s_l[h]);
+      part_o[pi * D + d] = num * inv;
+      if (d == 0) part_lse[pi] = M + __log2f(den);
     }
   }
 }
@@ -286,23 +382,20 @@ static int pow2_at_least(int g) {
 
 DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int max_context_len, int window,
                        int split_tokens) {
-  (void)D;
+  (void)Hq;
   DecodePlan p{};
-  const int G = Hq / Hkv;
-  const int GP = pow2_at_least(G);
-  const int cap = (kScoreFloats / GP) & ~15;
   const int span = window > 0 ? std::min(max_context_len, window + 15) : max_context_len;
   int C = split_tokens;
   if (C == 0) {
-    // Aim for about 8 workgroups per CU over the whole grid, splits of 128..cap tokens.
+    // About 2048 workgroups over the whole grid (8 per CU), splits of 256..4096 tokens in
+    // whole 64-token chunks.
     const long long target = 2048;
     long long want = ((long long)B * Hkv * span + target - 1) / target;
-    want = (want + 15) & ~15LL;
-    C = (int)std::max<long long>(128, std::min<long long>(want, cap));
+    want = (want + 63) & ~63LL;
+    C = (int)std::max<long long>(256, std::min<long long>(want, 4096));
   }
   p.split_tokens = C;
-  p.n_split = (span + C - 1) / C;
-  if (p.n_split < 1) p.n_split = 1;
+  p.n_split = std::max(1, (span + C - 1) / C);
   if (p.n_split == 1) {
     p.workspace_bytes = 0;
   } else {

@@ -18,6 +18,8 @@ struct PrefillArgs {
   int causal, window;
 };
 
+constexpr int kMaxSplitTokens = 8192;  // largest split_tokens a decode call accepts
+
 struct DecodePlan {
   int split_tokens;  // tokens per workgroup along the KV axis (multiple of 16)
   int n_split;       // workgroups per (sequence, KV head)

@@ -26,11 +26,25 @@
 //    applied only on tiles that straddle an edge. exp2 with scale*log2(e) folded into one FMA.
 #include "common.h"
 #include "launch.h"
+#include <type_traits>
 
 namespace attn {
 
 constexpr int kPrefillThreads = 256;
 constexpr int kBN = 64;  // keys per tile
+// The running max lags the true max by at most this much (log2 units), so probabilities stay
+// below 2^kRescaleSlack; O and l share the same reference, so o = O / l is unchanged.
+constexpr float kRescaleSlack = 8.0f;
+
+// max / sum over lanes l and l ^ 32 (the two halves of a 32x32 accumulator column)
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 template <int D>
 struct PrefillTile {
@@ -168,6 +182,79 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(
   }
   __syncthreads();
 
+  // One tile step for this wave. MASK selects the edge-tile variant (causal diagonal, window
+  // edge or the ragged end of the sequence); interior tiles skip all mask arithmetic.
+  auto tile_step = [&](const uint16_t* ks, const uint16_t* vs, int k0, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    // S^T = K Q^T
+    f32x16 sacc[kBN / 32];
+#pragma unroll
+    for (int kb = 0; kb < kBN / 32; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+      for (int t = 0; t < QSTEPS; ++t) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (32 * kb + col) * T::KPAD + 16 * t + 8 * half);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], sacc[kb], 0, 0, 0);
+      }
+    }
+    if constexpr (MASK) {
+      // register r of block kb holds key offset 32*kb + 8*(r/4) + (r%4) + 4*half of the tile
+      const int qp = q0w + col;
+      int hi = S - 1 - k0;
+      if (causal) hi = min(hi, qp - k0);
+      const int lo_off = window > 0 ? qp - window + 1 - k0 : -(1 << 30);
+      const int hi4 = hi - 4 * half, lo4 = lo_off - 4 * half;
+#pragma unroll
+      for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+          if (off > hi4 || off < lo4) sacc[kb][r] = -INFINITY;
+        }
+    }
+    // online softmax in the log2 domain; the running max is only moved (and the accumulator
+    // rescaled) when some row's max grows by more than kRescaleSlack, so most tiles skip it.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = xhalf_max(mx) * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+    }
+    float rs = 0.f;
+    bf16x8 pf[kBN / 16];
+#pragma unroll
+    for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = fast_exp2(fmaf(sacc[kb][r], scale_log2, -m_run));
+        const float p1 = fast_exp2(fmaf(sacc[kb][r + 1], scale_log2, -m_run));
+        rs += p0 + p1;
+        const bf16x2 pp = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
+        pf[2 * kb + (r >> 3)][r & 7] = pp[0];
+        pf[2 * kb + (r >> 3)][(r & 7) + 1] = pp[1];
+      }
+    l_run += xhalf_sum(rs);
+    // O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int u = 0; u < kBN / 16; ++u) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vs + (32 * db + col) * T::VPAD + 16 * u + 8 * half);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[u], oacc[db], 0, 0, 0);
+      }
+  };
+
   for (int j = jlo; j <= jhi; ++j) {
     const int st = (j - jlo) & 1;
     if (j < jhi) load_tile(j + 1);
@@ -177,69 +264,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(
     if (relevant) {
       const uint16_t* ks = smem + st * T::STAGE;
       const uint16_t* vs = ks + T::K_ELEMS;
-      // S^T = K Q^T
-      f32x16 sacc[kBN / 32];
-#pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-        for (int t = 0; t < QSTEPS; ++t) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (32 * kb + col) * T::KPAD + 16 * t + 8 * half);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], sacc[kb], 0, 0, 0);
-        }
-      }
-      // mask on edge tiles: accumulator register r of block kb holds key
-      // 32*kb + 8*(r/4) + 4*half + r%4 for query q0w + col.
       const bool full = (!causal || k0 + kBN - 1 <= q0w) &&
                         (window == 0 || qw_last - k0 < window) && (k0 + kBN <= S);
-      if (!full) {
-        const int qp = q0w + col;
-#pragma unroll
-        for (int kb = 0; kb < kBN / 32; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-            bool vis = key < S;
-            if (causal) vis = vis && key <= qp;
-            if (window > 0) vis = vis && qp - key < window;
-            if (!vis) sacc[kb][r] = -INFINITY;
-          }
-      }
-      // online softmax (log2 domain, scale folded into the exponent's FMA)
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * scale_log2);
-      const float alpha = fast_exp2(m_run - m_new);
-      float rs = 0.f;
-      bf16x8 pf[kBN / 16];
-#pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(sacc[kb][r], scale_log2, -m_new));
-          rs += p;
-          pf[2 * kb + (r >> 3)][r & 7] = (__bf16)p;
-        }
-      rs += __shfl_xor(rs, 32);
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-#pragma unroll
-      for (int i = 0; i < DB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
-      // O^T += V^T P^T
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int u = 0; u < kBN / 16; ++u) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vs + (32 * db + col) * T::VPAD + 16 * u + 8 * half);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[u], oacc[db], 0, 0, 0);
-        }
+      if (full)
+        tile_step(ks, vs, k0, std::false_type{});
+      else
+        tile_step(ks, vs, k0, std::true_type{});
     }
 
     if (j < jhi) store_tile(st ^ 1);

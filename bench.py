@@ -3,7 +3,8 @@
 One step = one pass of the whole path on the Llama-3.2-1B-shaped workload:
   1. kv_cache_append of the newest token of each of 64 sequences into the paged bf16 cache
      (32 query heads, 8 KV heads, D = 64, block 16, contexts uniform in [512, 4096]),
-  2. a 512 MiB scratch write that evicts L2 and the Infinity Cache (so decode reads HBM),
+  2. a 512 MiB scratch read that evicts L2 and the Infinity Cache with clean lines (so the
+     decode reads its cache from HBM, and no dirty write-back overlaps it),
   3. attn_decode_paged over that cache (split-KV + log-sum-exp merge),
   4. attn_prefill: causal GQA prefill, batch 1, S = 4096, 32/8 heads, D = 64, bf16.
 Each call is bracketed by HIP events on the stream the library launches on. The headline
@@ -138,7 +139,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama1b", choices=["llama1b", "swa", "int8_70b"])
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0 = skip)")
-    ap.add_argument("--no-flush", action="store_true", help="skip the cache-evicting scratch write")
+    ap.add_argument("--no-flush", action="store_true", help="skip the cache-evicting scratch read")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -158,7 +159,7 @@ def main(argv=None):
 
     P = setup_prefill(t, pwl) if pwl else None
     Dd = setup_decode(t, dwl)
-    flush = t.empty(512 * 1024 * 1024 // 4, dtype=t.float32, device="cuda")
+    flush = t.ones(512 * 1024 * 1024 // 4, dtype=t.float32, device="cuda")
     t.cuda.synchronize()
 
     def step(ev=None):
@@ -168,7 +169,7 @@ def main(argv=None):
                           k_scale=Dd["ks"], v_scale=Dd["vs"])
         if "a1" in e: e["a1"].record()
         if not args.no_flush:
-            flush.fill_(1.0)
+            flush.sum()
         if "d0" in e: e["d0"].record()
         A.attn_decode_paged(Dd["q"], Dd["kc"], Dd["vc"], Dd["table"], Dd["ctx"], dwl.ctx_hi,
                             k_scale=Dd["ks"], v_scale=Dd["vs"], scale=dwl.scale, window=dwl.window,

@@ -104,7 +104,8 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_context
  *                 KV range across workgroups without reading device memory.
  *  window       : 0 = no window; else only the last `window` positions are attended.
  *  split_tokens : tokens per workgroup along the KV axis: 0 = the library's choice, else a
- *                 positive multiple of block_size. Partials are merged by log-sum-exp.
+ *                 positive multiple of block_size, at most 8192 (ATTN_ERR_UNSUPPORTED above).
+ *                 Partials are merged by log-sum-exp.
  *  workspace    : device buffer of at least attn_decode_workspace_size(...) bytes (may be NULL
  *                 when that size is 0); overwritten by the call; its contents on entry do not
  *                 matter. Two calls in flight at once must not share a workspace.

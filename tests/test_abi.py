@@ -82,7 +82,7 @@ def _decode(**kw):
     (dict(ks=FAKE, vs=FAKE), A.ATTN_ERR_SHAPE), (dict(Hq=6, Hkv=4), A.ATTN_ERR_SHAPE),
     (dict(maxctx=0), A.ATTN_ERR_SHAPE), (dict(window=-2), A.ATTN_ERR_SHAPE), (dict(split=-16), A.ATTN_ERR_SHAPE),
     (dict(split=24), A.ATTN_ERR_SHAPE), (dict(D=80), A.ATTN_ERR_UNSUPPORTED), (dict(bs=8), A.ATTN_ERR_UNSUPPORTED),
-    (dict(Hq=34, Hkv=2), A.ATTN_ERR_UNSUPPORTED), (dict(split=4096), A.ATTN_ERR_UNSUPPORTED),
+    (dict(Hq=34, Hkv=2), A.ATTN_ERR_UNSUPPORTED), (dict(split=8208), A.ATTN_ERR_UNSUPPORTED),
     (dict(maxctx=5000, split=64), A.ATTN_ERR_WORKSPACE),
     (dict(maxctx=5000, split=64, ws=FAKE, wsb=16), A.ATTN_ERR_WORKSPACE),
 ])
