@@ -13,17 +13,22 @@
 //  * A workgroup is 4 waves; a wave owns 32 query rows of one head. The waves of a workgroup
 //    are the query heads that share one KV head (GQA) and/or consecutive 32-row chunks, so one
 //    K/V tile in LDS serves 128 query rows.
+//  * K and V tiles (64 keys) move from global memory straight into LDS with
+//    global_load_lds_dwordx4 (no register staging), double-buffered: the next tile's loads are
+//    in flight while the current tile is computed; one barrier per tile. Both tiles keep their
+//    natural [key][d] rows; 16-byte chunks are XOR-swizzled by key so the MFMA operand reads
+//    below are free of LDS bank conflicts.
 //  * Scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16: A = 32 keys of
-//    the K tile (LDS, [key][d] rows), B = Q^T held in registers for the whole kernel. In the
-//    accumulator each lane then owns one query column, so the row max / row sum are in-lane
-//    reductions plus one exchange between the two 32-lane halves.
+//    the K tile, B = Q^T held in registers for the whole kernel. Each lane then owns one query
+//    column, so the row max / row sum are in-lane reductions plus one exchange between the two
+//    32-lane halves (v_permlane32_swap).
 //  * P^T (bf16) goes straight from the score accumulator into the B operand of the PV MFMA,
-//    O^T += V^T P^T; V is stored transposed in LDS ([d][key]) with the key slots of every
-//    16-key group permuted so that each lane's 8 keys are contiguous (one 16-byte LDS read).
-//  * K/V tiles are double-buffered in LDS; the next tile's global loads are in flight while
-//    the current one is computed; one barrier per tile.
+//    O^T += V^T P^T. The V^T operand is read from the natural V tile with ds_read_b64_tr_b16
+//    (each lane receives 4 consecutive keys of one d), addressed so that its keys line up with
+//    the keys the score accumulator put in the same lane.
 //  * Tiles entirely hidden by the causal mask or the window are never visited; the mask is
-//    applied only on tiles that straddle an edge. exp2 with scale*log2(e) folded into one FMA.
+//    applied only on tiles that straddle an edge. exp2 with scale*log2(e) folded into one FMA;
+//    the running max moves only when it grows by more than kRescaleSlack.
 #include "common.h"
 #include "launch.h"
 #include <type_traits>
@@ -46,33 +51,58 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D>
-struct PrefillTile {
-  static constexpr int KPAD = D + 8;      // K row pitch in LDS (elements)
-  static constexpr int VPAD = kBN + 8;    // V^T row pitch in LDS (elements)
-  static constexpr int K_ELEMS = kBN * KPAD;
-  static constexpr int V_ELEMS = D * VPAD;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int K_CHUNKS = kBN * D / 8;          // 16-byte chunks of a K tile
-  static constexpr int K_PER_THREAD = K_CHUNKS / kPrefillThreads;
-  static constexpr int V_ITEMS = (kBN / 4) * (D / 8);   // 4 keys x 8 d items of a V tile
-};
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short i16x4 __attribute__((vector_size(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// Slot of key offset o (0..15) inside its 16-key group of a V^T row: bits 2 and 3 swapped.
-__device__ __forceinline__ int vt_slot(int o) {
-  return (o & 3) | ((o & 4) << 1) | ((o & 8) >> 1);
+// One global_load_lds_dwordx4: each lane copies 16 bytes from `g` to LDS byte address
+// lds_off + 16 * lane. Written as asm so the compiler does not treat every later LDS read as
+// a possible alias of the in-flight copy (it would wait for the copy before the current
+// tile's reads); completion is awaited explicitly with vmcnt(0) before the next barrier. The
+// instruction writes no registers.
+__device__ __forceinline__ void lds_dma_16(const void* g, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_off), "v"(g)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void*)p;
 }
 
 template <int D>
-__global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(
+struct PTile {
+  static constexpr int ROWB = D * 2;                 // bytes of one K or V row
+  static constexpr int CHUNKS = ROWB / 16;           // 16-byte chunks per row
+  static constexpr int TILE = kBN * ROWB;            // bytes of one K (or V) tile
+  static constexpr int STAGE = 2 * TILE;             // K tile then V tile
+  static constexpr int INSTR = TILE / 1024;          // wave load instructions per tile
+  static constexpr int PER_WAVE = INSTR / 4;         // ... per wave
+  static constexpr int ROWS_PER_INSTR = 1024 / ROWB;
+};
+
+// Chunk swizzles (c = 16-byte chunk index inside a row). K: the 16 lanes of a ds_read_b128 pass
+// read one chunk of 16 consecutive keys; V: a ds_read_b64_tr_b16 pass reads 64 bytes of 4
+// consecutive keys. Both land on distinct 4-bank groups.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
+
+template <int D>
+__global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int S,
     int Hq, int Hkv, int G, int HW, int QW, int n_qblk, int n_hsub, float scale_log2,
     int causal, int window) {
-  using T = PrefillTile<D>;
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  using T = PTile<D>;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;  // query column inside the wave's 32 rows
   const int half = lane >> 5;
 
@@ -123,68 +153,59 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
   float m_run = kNegBig, l_run = 0.f;
 
-  // ---- global -> register staging of one K/V tile ---------------------------------------
-  const int64_t kv_row_stride = (int64_t)Hkv * D;  // elements between consecutive keys
+  // ---- direct global -> LDS tile loads ---------------------------------------------------
+  // Wave instruction n (of INSTR per tile) writes LDS bytes [1024n, 1024n + 1024) of the tile;
+  // this wave issues n = wave + 4i. Lane l fills LDS row r = n*ROWS_PER_INSTR + l / CHUNKS,
+  // swizzled chunk l % CHUNKS, i.e. global chunk (l % CHUNKS) ^ swz(r). The swizzles depend on
+  // r only through bits that are the same for every i, so each lane has one fixed chunk.
+  const int64_t kv_row_stride = (int64_t)Hkv * D;
   const uint16_t* kbase = k + ((int64_t)b * S * Hkv + g) * D;
   const uint16_t* vbase = v + ((int64_t)b * S * Hkv + g) * D;
-  u32x4 kst[T::K_PER_THREAD];
-  u32x4 vst[4];
-  const bool v_thread = tid < T::V_ITEMS;
-  const int v_kq = tid / (D / 8), v_dc = tid % (D / 8);
+  const int ld_row0 = wave * T::ROWS_PER_INSTR + lane / T::CHUNKS;
+  const int ld_kchunk = (lane % T::CHUNKS) ^ k_swz<D>(ld_row0);
+  const int ld_vchunk = (lane % T::CHUNKS) ^ v_swz<D>(ld_row0);
+  constexpr int ROW_STEP = 4 * T::ROWS_PER_INSTR;  // rows between this wave's instructions
 
-  auto load_tile = [&](int j) {
+  auto issue_tile = [&](int j, int stage) {
     const int k0 = j * kBN;
+    char* kdst = smem + stage * T::STAGE + wave * 1024;
+    char* vdst = kdst + T::TILE;
 #pragma unroll
-    for (int i = 0; i < T::K_PER_THREAD; ++i) {
-      const int id2 = tid + kPrefillThreads * i;
-      const int key = id2 / (D / 8), dc = id2 % (D / 8);
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (k0 + key < S) w = *reinterpret_cast<const u32x4*>(kbase + (k0 + key) * kv_row_stride + 8 * dc);
-      kst[i] = w;
-    }
-    if (v_thread) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = k0 + 4 * v_kq + r;
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (key < S) w = *reinterpret_cast<const u32x4*>(vbase + key * kv_row_stride + 8 * v_dc);
-        vst[r] = w;
-      }
-    }
-  };
-  auto store_tile = [&](int stage) {
-    uint16_t* ks = smem + stage * T::STAGE;
-    uint16_t* vs = ks + T::K_ELEMS;
-#pragma unroll
-    for (int i = 0; i < T::K_PER_THREAD; ++i) {
-      const int id2 = tid + kPrefillThreads * i;
-      const int key = id2 / (D / 8), dc = id2 % (D / 8);
-      *reinterpret_cast<u32x4*>(ks + key * T::KPAD + 8 * dc) = kst[i];
-    }
-    if (v_thread) {
-      const int kk = 4 * v_kq;  // first key of the quad inside the tile
-      const int slot = (kk & ~15) + vt_slot(kk & 15);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int wi = e >> 1;
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        u32x2 pr;
-        pr[0] = __builtin_amdgcn_perm(vst[1][wi], vst[0][wi], sel);
-        pr[1] = __builtin_amdgcn_perm(vst[3][wi], vst[2][wi], sel);
-        *reinterpret_cast<u32x2*>(vs + (8 * v_dc + e) * T::VPAD + slot) = pr;
-      }
+    for (int i = 0; i < T::PER_WAVE; ++i) {
+      const int row = min(k0 + ld_row0 + i * ROW_STEP, S - 1);  // rows past S: any valid row
+      const int64_t roff = (int64_t)row * kv_row_stride;
+      lds_dma_16(kbase + roff + 8 * ld_kchunk, lds_addr(kdst + i * 4096));
+      lds_dma_16(vbase + roff + 8 * ld_vchunk, lds_addr(vdst + i * 4096));
     }
   };
 
-  if (jlo <= jhi) {
-    load_tile(jlo);
-    store_tile(0);
+  // ---- LDS operand addresses (bytes, relative to a stage) --------------------------------
+  // K A-operand of step t, block kb: row 32kb + col, chunk (2t + half) ^ k_swz(col).
+  int kaddr_t[QSTEPS];
+  {
+    const int s = k_swz<D>(col);
+#pragma unroll
+    for (int t = 0; t < QSTEPS; ++t) kaddr_t[t] = col * T::ROWB + 16 * ((2 * t + half) ^ s);
   }
-  __syncthreads();
+  // V^T A-operand via ds_read_b64_tr_b16. Lane group m = lane/16 (h = m/2, dh = m%2), lane i
+  // in the group addresses row 16u + 8r + 4h + i/4 and elements 32db + 16dh + 4(i%4) .. +3;
+  // it then receives keys 16u + 8r + 4h + 0..3 of d = 32db + 16dh + i, which are the keys the
+  // score accumulator holds in elements 4r..4r+3 of this lane's P^T fragment for step u.
+  int vaddr_db[DB];
+  {
+    const int m = lane >> 4, i = lane & 15;
+    const int h = m >> 1, dh = m & 1;
+    const int row = 4 * h + (i >> 2);  // + 16u + 8r (multiples of 4: swizzle unchanged)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int c = 4 * db + 2 * dh + ((i & 3) >> 1);
+      vaddr_db[db] = T::TILE + row * T::ROWB + 16 * (c ^ v_swz<D>(row)) + 8 * (i & 1);
+    }
+  }
 
   // One tile step for this wave. MASK selects the edge-tile variant (causal diagonal, window
   // edge or the ragged end of the sequence); interior tiles skip all mask arithmetic.
-  auto tile_step = [&](const uint16_t* ks, const uint16_t* vs, int k0, auto mask_tag) {
+  auto tile_step = [&](const char* st_base, int k0, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     // S^T = K Q^T
     f32x16 sacc[kBN / 32];
@@ -194,7 +215,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(
       for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
 #pragma unroll
       for (int t = 0; t < QSTEPS; ++t) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (32 * kb + col) * T::KPAD + 16 * t + 8 * half);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(st_base + kaddr_t[t] + kb * 32 * T::ROWB);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], sacc[kb], 0, 0, 0);
       }
     }
@@ -213,8 +234,6 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(
           if (off > hi4 || off < lo4) sacc[kb][r] = -INFINITY;
         }
     }
-    // online softmax in the log2 domain; the running max is only moved (and the accumulator
-    // rescaled) when some row's max grows by more than kRescaleSlack, so most tiles skip it.
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb)
@@ -250,30 +269,33 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int u = 0; u < kBN / 16; ++u) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vs + (32 * db + col) * T::VPAD + 16 * u + 8 * half);
+        const char* p = st_base + vaddr_db[db] + u * 16 * T::ROWB;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * T::ROWB));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[u], oacc[db], 0, 0, 0);
       }
   };
 
+  if (jlo <= jhi) issue_tile(jlo, 0);
+
   for (int j = jlo; j <= jhi; ++j) {
     const int st = (j - jlo) & 1;
-    if (j < jhi) load_tile(j + 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile-j loads have landed
+    __syncthreads();                     // ... and everyone's; stage st^1 is no longer read
+    if (j < jhi) issue_tile(j + 1, st ^ 1);
 
     const int k0 = j * kBN;
     const bool relevant = wave_live && k0 <= kmax_w && k0 + kBN - 1 >= kmin_w;
     if (relevant) {
-      const uint16_t* ks = smem + st * T::STAGE;
-      const uint16_t* vs = ks + T::K_ELEMS;
+      const char* st_base = smem + st * T::STAGE;
       const bool full = (!causal || k0 + kBN - 1 <= q0w) &&
                         (window == 0 || qw_last - k0 < window) && (k0 + kBN <= S);
       if (full)
-        tile_step(ks, vs, k0, std::false_type{});
+        tile_step(st_base, k0, std::false_type{});
       else
-        tile_step(ks, vs, k0, std::true_type{});
+        tile_step(st_base, k0, std::true_type{});
     }
-
-    if (j < jhi) store_tile(st ^ 1);
-    __syncthreads();
   }
 
   // ---- epilogue: O = O^T / l, bf16 RNE ---------------------------------------------------
@@ -296,7 +318,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(
   }
 }
 
-int launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
+template <int D>
+static void launch_d(const PrefillArgs& a, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
   const int HW = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;  // heads per workgroup
   const int QW = 4 / HW;                                    // 32-row chunks per head
@@ -305,19 +328,24 @@ int launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
   const int n_hsub = G / HW;
   const long long nwg = (long long)a.B * a.Hkv * n_hsub * n_qblk;
   const float scale_log2 = a.scale * kLog2e;
-  if (a.D == 64) {
-    const size_t lds = 2 * PrefillTile<64>::STAGE * sizeof(uint16_t);
-    hipLaunchKernelGGL(prefill_bf16_kernel<64>, dim3((unsigned)nwg), dim3(kPrefillThreads), lds,
-                       stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (uint16_t*)a.o, a.lse, a.S, a.Hq, a.Hkv, G, HW, QW, n_qblk, n_hsub,
-                       scale_log2, a.causal, a.window);
-  } else {
-    const size_t lds = 2 * PrefillTile<128>::STAGE * sizeof(uint16_t);
-    hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3((unsigned)nwg), dim3(kPrefillThreads), lds,
-                       stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (uint16_t*)a.o, a.lse, a.S, a.Hq, a.Hkv, G, HW, QW, n_qblk, n_hsub,
-                       scale_log2, a.causal, a.window);
+  const size_t lds = 2 * PTile<D>::STAGE;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipFuncSetAttribute((const void*)prefill_bf16_kernel<D>,
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    attr_set = true;
   }
+  hipLaunchKernelGGL(prefill_bf16_kernel<D>, dim3((unsigned)nwg), dim3(kPrefillThreads), lds,
+                     stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (uint16_t*)a.o, a.lse, a.S, a.Hq, a.Hkv, G, HW, QW, n_qblk, n_hsub,
+                     scale_log2, a.causal, a.window);
+}
+
+int launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
+  if (a.D == 64)
+    launch_d<64>(a, stream);
+  else
+    launch_d<128>(a, stream);
   return 0;
 }
 
