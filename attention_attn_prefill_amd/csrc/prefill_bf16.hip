@@ -106,14 +106,25 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(
   const int col = lane & 31;  // query column inside the wave's 32 rows
   const int half = lane >> 5;
 
-  // ---- workgroup -> (b, kv head, head sub-group, query block); longest blocks first --------
-  int id = blockIdx.x;
-  const int qblk_rank = id % n_qblk;
-  id /= n_qblk;
-  const int hsub = id % n_hsub;
-  id /= n_hsub;
-  const int g = id % Hkv;
-  const int b = id / Hkv;
+  // ---- workgroup -> (b, kv head, head sub-group, query block) -----------------------------
+  // Consecutive workgroup ids are dispatched round-robin over the 8 XCDs, each with its own L2.
+  // When the number of (b, kv head, head sub-group) groups is a multiple of 8, group gi runs
+  // entirely on XCD gi % 8, so its K/V stream is fetched into one L2 and reused there; inside
+  // an XCD the query blocks still go longest first.
+  const int n_groups = gridDim.x / n_qblk;
+  int gi, qblk_rank;
+  if ((n_groups & 7) == 0) {
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int per_xcd = n_groups >> 3;
+    qblk_rank = slot / per_xcd;
+    gi = xcd + 8 * (slot % per_xcd);
+  } else {
+    qblk_rank = blockIdx.x % n_qblk;
+    gi = blockIdx.x / n_qblk;
+  }
+  const int hsub = gi % n_hsub;
+  const int g = (gi / n_hsub) % Hkv;
+  const int b = gi / (n_hsub * Hkv);
   const int qblk = causal ? (n_qblk - 1 - qblk_rank) : qblk_rank;
 
   const int rows = 32 * QW;
