@@ -51,6 +51,13 @@ __device__ __forceinline__ V ld_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
 }
 
+// INT8 -> fp16 widening without conversions: with u = x ^ 0x80 (= x + 128 as a byte), the
+// fp16 bit pattern 0x64uu is exactly 1024 + u = 1152 + x. One v_perm builds two such halves
+// from a dword of codes (the 0x64 bytes come from the constant operand).
+__device__ __forceinline__ uint32_t widen_lo(uint32_t u) { return __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u); }
+__device__ __forceinline__ uint32_t widen_hi(uint32_t u) { return __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u); }
+constexpr float kI8Bias = 1152.0f;
+
 // xor-16 / xor-32 lane partners within a wave
 __device__ __forceinline__ float max_x32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -86,13 +93,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     int n_split) {
   using SH = DecodeShape<D, I8>;
   constexpr int BS = SH::BS, U = SH::U, CT = U * BS;  // CT tokens per chunk
-  __shared__ float s_p[kDecodeWaves][CT][GP];       // probabilities handed to the PV lanes
+  // probabilities handed from the MFMA lanes to the PV lanes: fp32 [token][head] for bf16;
+  // for INT8, fp16 pairs (token t, token t + 8) of p' = p * v_scale, [block][pair][head]
+  __shared__ float s_p[kDecodeWaves][I8 ? 1 : CT][GP];
+  __shared__ uint32_t s_pp[kDecodeWaves][I8 ? U : 1][8][GP];
   __shared__ float s_alpha[kDecodeWaves][GP];
   __shared__ float s_red[kDecodeWaves][GP][D];
-  __shared__ float s_ml[kDecodeWaves][2][GP];
+  __shared__ float s_ml[kDecodeWaves][3][GP];
   __shared__ int s_pb[kMaxSplitBlocks];  // the split's slice of the block table
 
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // Grid (Hkv, B, n_split) with the split index slowest and reversed: consecutive workgroups
+  // (dispatched round-robin over the XCDs) then belong to different sequences, so the XCDs
+  // share ragged work evenly; splits that exist only for long contexts go first.
+  const int split = n_split - 1 - blockIdx.z, g = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -122,17 +135,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
 
   // MFMA (QK^T) lane roles: column = query head, rows = 4 tokens of the block
   const int hq = lane & 15, grp = lane >> 4;
-  // PV lane roles: 8 consecutive d of one token
+  // PV lane roles: 8 consecutive d of one token (bf16) or of a token pair (INT8)
   const int c8 = lane % SH::CPR, ts = lane / SH::CPR;
 
   typedef typename std::conditional<I8, f16x8, bf16x8>::type frag_t;
   frag_t qf[SH::KSTEPS];
+  float qsum = 0.f;  // INT8: sum of this head's fp16 q values (the widened codes carry +1152)
   {
     const uint16_t* qrow = q + ((int64_t)b * Hq + g * G + hq) * D;
 #pragma unroll
     for (int j = 0; j < SH::KSTEPS; ++j) {
-      // bf16: step j covers d = 32j + 8*grp + e; int8: one 16-byte load feeds steps 2jj, 2jj+1
-      // covering d = 64*jj + 16*grp + 8*sub + e.
+      // bf16: step j covers d = 32j + 8*grp + e; INT8: one 16-byte load feeds steps 2jj,
+      // 2jj+1 covering d = 64*jj + 16*grp + 8*sub + e.
       const int d0 = I8 ? (64 * (j / 2) + 16 * grp + 8 * (j % 2)) : (32 * j + 8 * grp);
       u32x4 w = {0u, 0u, 0u, 0u};
       if (hq < G) w = *reinterpret_cast<const u32x4*>(qrow + d0);
@@ -141,15 +155,22 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
         for (int e = 0; e < 4; ++e) {
           qf[j][2 * e] = (_Float16)bf16_lo(w[e]);
           qf[j][2 * e + 1] = (_Float16)bf16_hi(w[e]);
+          qsum += (float)qf[j][2 * e] + (float)qf[j][2 * e + 1];
         }
       } else {
         qf[j] = __builtin_bit_cast(bf16x8, w);
       }
     }
+    if constexpr (I8) {
+      qsum += __shfl_xor(qsum, 16);
+      qsum = sum_x32(qsum);
+    }
   }
+  const float bias = kI8Bias * qsum;
 
   float m_run = kNegBig;  // per head (lanes hq), log2 units
   float l_part = 0.f;     // this lane's share of the row sum
+  float ps_part = 0.f;    // INT8: this lane's share of sum(p'), in the fp16 values used
   float acc[GP][8];
 #pragma unroll
   for (int h = 0; h < GP; ++h)
@@ -172,7 +193,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     u32x4 kw[U][SH::KLOADS];
     typedef typename std::conditional<I8, u32x2, u32x4>::type vword_t;
     vword_t vw[U][SH::VLOADS];
-    float ksc[U][4], vsc[U][SH::VLOADS];
+    float ksc[U][4], vsc[U][4];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t brow = pool_offset(pb[u], Hkv, g, BS, 0, D);
@@ -185,12 +206,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
 #pragma unroll
         for (int i = 0; i < SH::VLOADS; ++i)
           vw[u][i] = ld_stream<u32x2>(vc + (int64_t)(i * SH::TPW + ts) * D + 8 * c8);
-        const __half* ks = k_scale + ((int64_t)pb[u] * Hkv + g) * BS;
+        const int64_t srow = ((int64_t)pb[u] * Hkv + g) * BS + 4 * grp;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ksc[u][i] = __half2float(ks[4 * grp + i]);
-        const __half* vs = v_scale + ((int64_t)pb[u] * Hkv + g) * BS;
-#pragma unroll
-        for (int i = 0; i < SH::VLOADS; ++i) vsc[u][i] = __half2float(vs[i * SH::TPW + ts]);
+        for (int i = 0; i < 4; ++i) {
+          ksc[u][i] = __half2float(k_scale[srow + i]);
+          vsc[u][i] = __half2float(v_scale[srow + i]);
+        }
       } else {
         const uint16_t* kc = reinterpret_cast<const uint16_t*>(k_cache) + brow + (int64_t)hq * D;
 #pragma unroll
@@ -213,13 +234,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
         for (int jj = 0; jj < SH::KLOADS; ++jj)
 #pragma unroll
           for (int sub = 0; sub < 2; ++sub) {
-            f16x8 a;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const uint32_t word = kw[u][jj][2 * sub + e / 4];
-              a[e] = (_Float16)(int)(int8_t)(word >> (8 * (e % 4)));
-            }
-            a4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[2 * jj + sub], a4, 0, 0, 0);
+            const uint32_t w0 = kw[u][jj][2 * sub] ^ 0x80808080u;
+            const uint32_t w1 = kw[u][jj][2 * sub + 1] ^ 0x80808080u;
+            const u32x4 hv = {widen_lo(w0), widen_hi(w0), widen_lo(w1), widen_hi(w1)};
+            a4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, hv),
+                                                        qf[2 * jj + sub], a4, 0, 0, 0);
           }
       } else {
 #pragma unroll
@@ -230,8 +249,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
       for (int i = 0; i < 4; ++i) {
         const int t = t_begin + (blk0 + u) * BS + 4 * grp + i;
         const bool vis = okb[u] && t >= lo && t < t_end;
-        float s = a4[i] * scale_log2;
-        if constexpr (I8) s *= ksc[u][i];
+        float s;
+        if constexpr (I8)
+          s = (a4[i] - bias) * ksc[u][i] * scale_log2;
+        else
+          s = a4[i] * scale_log2;
         sc[u][i] = vis ? s : -INFINITY;
         cmax = fmaxf(cmax, sc[u][i]);
       }
@@ -244,6 +266,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
       const float alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
       l_part *= alpha;
+      ps_part *= alpha;
       if (grp == 0 && hq < GP) s_alpha[wave][hq] = alpha;
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -253,61 +276,110 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
         for (int e = 0; e < 8; ++e) acc[h][e] *= al;
       }
     }
-    // probabilities -> LDS [token][head]
+    // probabilities -> LDS
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float p = fast_exp2(sc[u][i] - m_run);
         l_part += p;
-        if (hq < GP) s_p[wave][u * BS + 4 * grp + i][hq] = p;
+        if constexpr (I8) {
+          // masked tokens: p = 0 exactly, and their (possibly NaN) scale is not used
+          const _Float16 pv16 = (_Float16)(sc[u][i] == -INFINITY ? 0.f : p * vsc[u][i]);
+          ps_part += (float)pv16;
+          const int t = 4 * grp + i;  // token inside block u: pair t & 7, element t >> 3
+          if (hq < GP)
+            reinterpret_cast<_Float16*>(&s_pp[wave][u][t & 7][hq])[t >> 3] = pv16;
+        } else {
+          if (hq < GP) s_p[wave][u * BS + 4 * grp + i][hq] = p;
+        }
       }
     __builtin_amdgcn_wave_barrier();
     // ---- PV on the VALU -----------------------------------------------------------------
+    if constexpr (I8) {
+      // lane (ts, c8) owns tokens ts + TPW*i of each block; it pairs t = ts + TPW*pr with t + 8
+      // and accumulates p'_t (1152 + x_t[d]) with v_dot2_f32_f16 (codes are finite, masked
+      // tokens have p' = 0)
+      constexpr int NPAIR = SH::VLOADS / 2;
+      static_assert(SH::TPW * NPAIR == 8, "token pairs are (t, t + 8)");
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int i = 0; i < SH::VLOADS; ++i) {
-        const int slot = i * SH::TPW + ts;
-        const int tpos = t_begin + (blk0 + u) * BS + slot;
-        if (!(okb[u] && tpos >= lo && tpos < t_end)) continue;  // masked slot may hold NaN
-        float x[8];
-        if constexpr (I8) {
+        for (int pr = 0; pr < NPAIR; ++pr) {
+          const int pair = ts + SH::TPW * pr;
+          const u32x2 bw = vw[u][pr], cw = vw[u][pr + NPAIR];
+          uint32_t xp[8];  // fp16 pairs (1152 + x_t, 1152 + x_{t+8}) for the lane's 8 d
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = (float)(int8_t)(vw[u][i][e / 4] >> (8 * (e % 4)));
-        } else {
+          for (int k = 0; k < 2; ++k) {
+            const uint32_t bx = bw[k] ^ 0x80808080u, cx = cw[k] ^ 0x80808080u;
+            const uint32_t i0 = __builtin_amdgcn_perm(cx, bx, 0x05010400u);  // b0 c0 b1 c1
+            const uint32_t i1 = __builtin_amdgcn_perm(cx, bx, 0x07030602u);  // b2 c2 b3 c3
+            xp[4 * k + 0] = widen_lo(i0);
+            xp[4 * k + 1] = widen_hi(i0);
+            xp[4 * k + 2] = widen_lo(i1);
+            xp[4 * k + 3] = widen_hi(i1);
+          }
+          uint32_t pp[GP];
+#pragma unroll
+          for (int h4 = 0; h4 < GP; h4 += 4) {
+            if constexpr (GP >= 4) {
+              const u32x4 p4 = *reinterpret_cast<const u32x4*>(&s_pp[wave][u][pair][h4]);
+              pp[h4] = p4[0]; pp[h4 + 1] = p4[1]; pp[h4 + 2] = p4[2]; pp[h4 + 3] = p4[3];
+            } else {
+#pragma unroll
+              for (int h = 0; h < GP; ++h) pp[h] = s_pp[wave][u][pair][h];
+            }
+          }
+#pragma unroll
+          for (int h = 0; h < GP; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              acc[h][e] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pp[h]),
+                                                 __builtin_bit_cast(f16x2, xp[e]), acc[h][e], false);
+        }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < SH::VLOADS; ++i) {
+          const int slot = i * SH::TPW + ts;
+          const int tpos = t_begin + (blk0 + u) * BS + slot;
+          if (!(okb[u] && tpos >= lo && tpos < t_end)) continue;  // masked slot may hold NaN
+          float x[8];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             x[2 * e] = bf16_lo(vw[u][i][e]);
             x[2 * e + 1] = bf16_hi(vw[u][i][e]);
           }
-        }
-        float pv[GP];
+          float pv[GP];
 #pragma unroll
-        for (int h4 = 0; h4 < GP; h4 += 4) {
-          if constexpr (GP >= 4) {
-            const f32x4 p4 = *reinterpret_cast<const f32x4*>(&s_p[wave][u * BS + slot][h4]);
-            pv[h4] = p4[0]; pv[h4 + 1] = p4[1]; pv[h4 + 2] = p4[2]; pv[h4 + 3] = p4[3];
-          } else {
+          for (int h4 = 0; h4 < GP; h4 += 4) {
+            if constexpr (GP >= 4) {
+              const f32x4 p4 = *reinterpret_cast<const f32x4*>(&s_p[wave][u * BS + slot][h4]);
+              pv[h4] = p4[0]; pv[h4 + 1] = p4[1]; pv[h4 + 2] = p4[2]; pv[h4 + 3] = p4[3];
+            } else {
 #pragma unroll
-            for (int h = 0; h < GP; ++h) pv[h] = s_p[wave][u * BS + slot][h];
+              for (int h = 0; h < GP; ++h) pv[h] = s_p[wave][u * BS + slot][h];
+            }
           }
-        }
 #pragma unroll
-        for (int h = 0; h < GP; ++h) {
-          float p = pv[h];
-          if constexpr (I8) p *= vsc[u][i];
+          for (int h = 0; h < GP; ++h)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, x[e], acc[h][e]);
+            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pv[h], x[e], acc[h][e]);
         }
-      }
-    __builtin_amdgcn_wave_barrier();  // s_p is rewritten by the next chunk
+    }
+    __builtin_amdgcn_wave_barrier();  // the staging slices are rewritten by the next chunk
   }
 
   // ---- reduce inside the wave ------------------------------------------------------------
-  // row sum: lanes hq, hq+16, hq+32, hq+48
+  // row sums: lanes hq, hq+16, hq+32, hq+48
   float l_w = l_part + __shfl_xor(l_part, 16);
   l_w = sum_x32(l_w);
+  float ps_w = 0.f;
+  if constexpr (I8) {
+    ps_w = ps_part + __shfl_xor(ps_part, 16);
+    ps_w = sum_x32(ps_w);
+  }
   // PV accumulators: lanes with equal c8
 #pragma unroll
   for (int h = 0; h < GP; ++h)
@@ -315,15 +387,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     for (int e = 0; e < 8; ++e)
 #pragma unroll
       for (int o = SH::CPR; o < 64; o <<= 1) acc[h][e] += __shfl_xor(acc[h][e], o);
-  if (ts == 0) {
-#pragma unroll
-    for (int h = 0; h < GP; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s_red[wave][h][8 * c8 + e] = acc[h][e];
-  }
   if (grp == 0 && hq < GP) {
     s_ml[wave][0][hq] = m_run;
     s_ml[wave][1][hq] = l_w;
+    s_ml[wave][2][hq] = ps_w;
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (ts == 0) {
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+      const float corr = I8 ? kI8Bias * s_ml[wave][2][h] : 0.f;  // remove the +1152 of the codes
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_red[wave][h][8 * c8 + e] = acc[h][e] - corr;
+    }
   }
   __syncthreads();
 
@@ -394,12 +470,10 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int max_context_len, int w
   const int span = window > 0 ? std::min(max_context_len, window + 15) : max_context_len;
   int C = split_tokens;
   if (C == 0) {
-    // About 2048 workgroups over the whole grid (8 per CU), splits of 256..4096 tokens in
-    // whole 64-token chunks.
-    const long long target = 2048;
-    long long want = ((long long)B * Hkv * span + target - 1) / target;
-    want = (want + 63) & ~63LL;
-    C = (int)std::max<long long>(256, std::min<long long>(want, 4096));
+    // Splits of about 1024 tokens (a quarter of the span for shorter contexts, at least 256):
+    // enough workgroups to balance ragged contexts over the CUs, few enough that the per-split
+    // prologue and the merge stay small.
+    C = std::min(1024, std::max(256, ((span / 4) + 255) & ~255));
   }
   p.split_tokens = C;
   p.n_split = std::max(1, (span + C - 1) / C);
@@ -427,7 +501,7 @@ int launch_decode(const DecodeArgs& a, hipStream_t stream) {
     part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(a.workspace) + lse_off);
   }
   const float scale_log2 = a.scale * kLog2e;
-  dim3 grid(ns, a.Hkv, a.B);
+  dim3 grid(a.Hkv, a.B, ns);
 #define ATTN_DSPLIT(DD, GG, I8)                                                                 \
   hipLaunchKernelGGL((decode_split_kernel<DD, GG, I8>), grid, dim3(kDecodeThreads), 0, stream, \
                      (const uint16_t*)a.q, a.k_cache, a.v_cache, (const __half*)a.k_scale,      \
