@@ -41,6 +41,8 @@ constexpr int kBN = 64;  // keys per tile
 // below 2^kRescaleSlack; O and l share the same reference, so o = O / l is unchanged.
 constexpr float kRescaleSlack = 8.0f;
 
+__device__ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
+
 // max / sum over lanes l and l ^ 32 (the two halves of a 32x32 accumulator column)
 __device__ __forceinline__ float xhalf_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -177,16 +179,35 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(
   const int ld_vchunk = (lane % T::CHUNKS) ^ v_swz<D>(ld_row0);
   constexpr int ROW_STEP = 4 * T::ROWS_PER_INSTR;  // rows between this wave's instructions
 
+  // Per-lane element offsets of this wave's rows at k0 = 0; a tile adds k0 * row stride (one
+  // wave-uniform 64-bit product). Only a tile that runs past S clamps rows, to S - 1 (any valid
+  // row will do: keys past S are masked).
+  int64_t koff[T::PER_WAVE], voff[T::PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < T::PER_WAVE; ++i) {
+    koff[i] = (int64_t)(ld_row0 + i * ROW_STEP) * kv_row_stride + 8 * ld_kchunk;
+    voff[i] = (int64_t)(ld_row0 + i * ROW_STEP) * kv_row_stride + 8 * ld_vchunk;
+  }
   auto issue_tile = [&](int j, int stage) {
     const int k0 = j * kBN;
     char* kdst = smem + stage * T::STAGE + wave * 1024;
     char* vdst = kdst + T::TILE;
+    if (k0 + kBN <= S) {
+      const uint16_t* kt = kbase + (int64_t)k0 * kv_row_stride;
+      const uint16_t* vt = vbase + (int64_t)k0 * kv_row_stride;
 #pragma unroll
-    for (int i = 0; i < T::PER_WAVE; ++i) {
-      const int row = min(k0 + ld_row0 + i * ROW_STEP, S - 1);  // rows past S: any valid row
-      const int64_t roff = (int64_t)row * kv_row_stride;
-      lds_dma_16(kbase + roff + 8 * ld_kchunk, lds_addr(kdst + i * 4096));
-      lds_dma_16(vbase + roff + 8 * ld_vchunk, lds_addr(vdst + i * 4096));
+      for (int i = 0; i < T::PER_WAVE; ++i) {
+        lds_dma_16(kt + koff[i], lds_addr(kdst + i * 4096));
+        lds_dma_16(vt + voff[i], lds_addr(vdst + i * 4096));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < T::PER_WAVE; ++i) {
+        const int row = min(k0 + ld_row0 + i * ROW_STEP, S - 1);
+        const int64_t roff = (int64_t)row * kv_row_stride;
+        lds_dma_16(kbase + roff + 8 * ld_kchunk, lds_addr(kdst + i * 4096));
+        lds_dma_16(vbase + roff + 8 * ld_vchunk, lds_addr(vdst + i * 4096));
+      }
     }
   };
 
@@ -269,8 +290,9 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(
       for (int r = 0; r < 16; r += 2) {
         const float p0 = fast_exp2(fmaf(sacc[kb][r], scale_log2, -m_run));
         const float p1 = fast_exp2(fmaf(sacc[kb][r + 1], scale_log2, -m_run));
-        rs += p0 + p1;
         const bf16x2 pp = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
+        // row sum of the bf16-rounded probabilities, the values the PV MFMA uses
+        rs = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, rs, false);
         pf[2 * kb + (r >> 3)][r & 7] = pp[0];
         pf[2 * kb + (r >> 3)][(r & 7) + 1] = pp[1];
       }

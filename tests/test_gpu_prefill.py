@@ -8,6 +8,11 @@ from tests.gpu_util import BF16_TOL, F32_TOL, dev, dev_bf16, host_bits, host_f64
 
 pytestmark = pytest.mark.gpu
 
+# bf16 prefill normalises by l = sum of the bf16-rounded probabilities (the values the PV
+# contraction uses), each within a relative 2^-9 of the exact exp, so ln l -- and the reported
+# LSE -- is within 2^-9 (~0.00195) of the exact log-sum-exp; fp32 accumulation adds ~1e-6.
+LSE_TOL_BF16 = 4e-3
+
 
 def _run(wl, x, causal=None, window=None, lse=True):
     import attention_attn_prefill_amd as A
@@ -54,7 +59,7 @@ def test_prefill_bf16_small(B, S, Hq, Hkv, D, causal, window):
     o, L = _run(wl, x)
     ro, rl = oracle.attention(x["q"], x["k"], x["v"], wl.scale, causal, window)
     assert maxabs(host_f64(o), ro) <= BF16_TOL
-    assert maxabs(host_f64(L), rl) <= 1e-3
+    assert maxabs(host_f64(L), rl) <= LSE_TOL_BF16
 
 
 @pytest.mark.parametrize("B,S,Hq,Hkv,D", [(1, 100, 4, 4, 64), (1, 77, 8, 2, 128), (2, 1000, 32, 8, 64)])
@@ -105,7 +110,7 @@ def _sampled_check(wl, rows, heads):
             v = prefill_slab(wl, "v", b, h // G)
             ro, rl = oracle.attention_head(q, k, v, wl.scale, rows, wl.causal, wl.window)
             worst = max(worst, maxabs(got[b, rows, h], ro))
-            assert maxabs(gl[b, h, rows], rl) <= 1e-3
+            assert maxabs(gl[b, h, rows], rl) <= LSE_TOL_BF16
     assert worst <= BF16_TOL, worst
     return o
 
