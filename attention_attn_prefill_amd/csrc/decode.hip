@@ -68,12 +68,14 @@ __device__ __forceinline__ float sum_x32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Chunks of U blocks (U*16 tokens) are the unit of work of one wave: their K and V loads are
-// all issued before any of them is consumed.
+// Chunks of U blocks (U*16 tokens, 8 KB of K+V for the bf16 D=128 and INT8 caches, 8 KB for
+// bf16 D=64) are the unit of work of one wave: their K and V loads are all issued before any of
+// them is consumed. Small chunks keep register use low, so more waves stay resident and more
+// bytes are in flight per CU (measured better than larger per-wave batches).
 template <int D, bool I8>
 struct DecodeShape {
   static constexpr int BS = 16;
-  static constexpr int U = (D == 64 || I8) ? 4 : 2;       // blocks per chunk
+  static constexpr int U = (D == 64 || I8) ? 2 : 1;       // blocks per chunk
   static constexpr int KSTEPS = D / 32;                    // MFMA k-steps per block
   static constexpr int KLOADS = I8 ? D / 64 : D / 32;      // 16-byte K loads per lane per block
   static constexpr int VBYTES = I8 ? 8 : 16;               // bytes per lane per V load (8 elements)
@@ -470,10 +472,13 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int max_context_len, int w
   const int span = window > 0 ? std::min(max_context_len, window + 15) : max_context_len;
   int C = split_tokens;
   if (C == 0) {
-    // Splits of about 1024 tokens (a quarter of the span for shorter contexts, at least 256):
-    // enough workgroups to balance ragged contexts over the CUs, few enough that the per-split
-    // prologue and the merge stay small.
-    C = std::min(1024, std::max(256, ((span / 4) + 255) & ~255));
+    // 2048-token splits for long spans, 1024 otherwise (a quarter of the span, at least 256,
+    // for short contexts): enough workgroups to balance ragged contexts over the CUs, few
+    // enough that the per-split prologue and the merge stay small (measured on MI355X).
+    if (span >= 8192)
+      C = 2048;
+    else
+      C = std::min(1024, std::max(256, ((span / 4) + 255) & ~255));
   }
   p.split_tokens = C;
   p.n_split = std::max(1, (span + C - 1) / C);
