@@ -2,7 +2,7 @@
 
 Every computation runs in the HIP kernels of libattn.so; torch supplies device memory and the
 current stream. The names follow the C ABI in include/attn.h: attn_prefill,
-attn_decode_paged, kv_cache_append, attn_decode_workspace_size.
+attn_prefill_paged, attn_decode_paged, kv_cache_append, attn_decode_workspace_size.
 """
 from __future__ import annotations
 
@@ -23,6 +23,8 @@ _I = ctypes.c_int
 _SIGS = {
     "attn_prefill": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _I, _P]),
     "attn_decode_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I, _I]),
+    "attn_prefill_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
+                                _I, _I, ctypes.c_float, _I, _I, _P]),
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
                                ctypes.c_float, _I, _I, _P, ctypes.c_size_t, _P]),
     "kv_cache_append": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
@@ -102,6 +104,25 @@ def attn_prefill(q, k, v, *, scale: float | None = None, causal: bool = True, wi
     _check(lib().attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q),
                               B, S, Hq, Hkv, D, float(scale), int(bool(causal)), int(window),
                               _stream(q)))
+    return out
+
+
+def attn_prefill_paged(q, k_cache, v_cache, block_table, cu_q, context_lens, max_q_len: int, *,
+                       k_new=None, v_new=None, scale: float | None = None, causal: bool = True,
+                       window: int = 0, out=None, lse=None):
+    """Chunked prefill over a paged cache (bf16). q [total_q][Hq][D] packed by cu_q [B+1];
+    k_new/v_new [total_q][Hkv][D] are written into the cache first when given."""
+    import torch
+    total_q, Hq, D = q.shape
+    num_blocks, Hkv, bs, _ = k_cache.shape
+    B = cu_q.shape[0] - 1
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib().attn_prefill_paged(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(cu_q), _ptr(context_lens), _ptr(out), _ptr(lse), B, Hq, Hkv, D, bs,
+        block_table.shape[1], num_blocks, int(max_q_len), total_q,
+        float(D ** -0.5 if scale is None else scale), int(bool(causal)), int(window), _stream(q)))
     return out
 
 

@@ -16,13 +16,16 @@
 
 namespace attn {
 
-template <int D, bool I8>
+// VARLEN: rows are a packed chunk (sequence b owns rows cu_q[b] .. cu_q[b+1]-1, the last
+// positions of its ctx[b] tokens) instead of explicit (seq_idx, pos) pairs.
+template <int D, bool I8, bool VARLEN>
 __global__ __launch_bounds__(256) void kv_append_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ table, void* __restrict__ k_cache, void* __restrict__ v_cache,
     __half* __restrict__ k_scale, __half* __restrict__ v_scale, int64_t rows, int Hkv, int bs,
-    int num_seqs, int max_blocks, int num_blocks) {
+    int num_seqs, int max_blocks, int num_blocks, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ ctx) {
   constexpr int TPR = D / 8;  // threads per (token, head) row
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t row = gid / TPR;
@@ -35,8 +38,20 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
   bool valid = in_range;
   int pb = 0, slot = 0;
   if (valid) {
-    const int b = seq_idx[t];
-    const int p = pos[t];
+    int b, p;
+    if constexpr (VARLEN) {
+      int lo = 0, hi = num_seqs;  // largest b with cu_q[b] <= t
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu_q[mid] <= t) lo = mid; else hi = mid - 1;
+      }
+      b = lo;
+      const int q_len = b < num_seqs ? cu_q[b + 1] - cu_q[b] : 0;
+      p = b < num_seqs ? ctx[b] - q_len + (int)(t - cu_q[b]) : -1;
+    } else {
+      b = seq_idx[t];
+      p = pos[t];
+    }
     valid = b >= 0 && b < num_seqs && p >= 0 && p < max_blocks * bs;
     if (valid) {
       pb = table[(int64_t)b * max_blocks + p / bs];
@@ -92,19 +107,21 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
   }
 }
 
-int launch_kv_append(const AppendArgs& a, hipStream_t stream) {
+template <bool VARLEN>
+static int launch_append(const AppendArgs& a, const int32_t* cu_q, const int32_t* ctx,
+                         hipStream_t stream) {
   const int64_t rows = (int64_t)a.T * a.Hkv;
   const int tpr = a.D / 8;
   const int64_t threads = rows * tpr;
   const int block = 256;
   const int64_t grid = (threads + block - 1) / block;
   if (grid == 0) return 0;
-#define ATTN_APPEND(DD, I8)                                                                     \
-  hipLaunchKernelGGL((kv_append_kernel<DD, I8>), dim3((unsigned)grid), dim3(block), 0, stream, \
-                     (const uint16_t*)a.k_new, (const uint16_t*)a.v_new, a.seq_idx, a.pos,     \
-                     a.block_table, a.k_cache, a.v_cache, (__half*)a.k_scale,                  \
-                     (__half*)a.v_scale, rows, a.Hkv, a.block_size, a.num_seqs,                \
-                     a.max_blocks_per_seq, a.num_blocks)
+#define ATTN_APPEND(DD, I8)                                                                    \
+  hipLaunchKernelGGL((kv_append_kernel<DD, I8, VARLEN>), dim3((unsigned)grid), dim3(block), 0, \
+                     stream, (const uint16_t*)a.k_new, (const uint16_t*)a.v_new, a.seq_idx,    \
+                     a.pos, a.block_table, a.k_cache, a.v_cache, (__half*)a.k_scale,            \
+                     (__half*)a.v_scale, rows, a.Hkv, a.block_size, a.num_seqs,                 \
+                     a.max_blocks_per_seq, a.num_blocks, cu_q, ctx)
   if (a.D == 64) {
     if (a.int8) ATTN_APPEND(64, true); else ATTN_APPEND(64, false);
   } else {
@@ -112,6 +129,15 @@ int launch_kv_append(const AppendArgs& a, hipStream_t stream) {
   }
 #undef ATTN_APPEND
   return 0;
+}
+
+int launch_kv_append(const AppendArgs& a, hipStream_t stream) {
+  return launch_append<false>(a, nullptr, nullptr, stream);
+}
+
+int launch_kv_append_varlen(const AppendArgs& a, const int32_t* cu_q, const int32_t* ctx,
+                            hipStream_t stream) {
+  return launch_append<true>(a, cu_q, ctx, stream);
 }
 
 }  // namespace attn

@@ -76,6 +76,35 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, float* ls
   return check_launch("attn_prefill");
 }
 
+int attn_prefill_paged(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                       void* v_cache, const int32_t* block_table, const int32_t* cu_q,
+                       const int32_t* context_lens, void* o, float* lse, int B, int Hq, int Hkv,
+                       int D, int block_size, int max_blocks_per_seq, int num_blocks,
+                       int max_q_len, int total_q, float scale, int causal, int window,
+                       void* stream) {
+  if (total_q < 0) return fail(ATTN_ERR_SHAPE, "total_q %d < 0", total_q);
+  if (B < 1 || Hq < 1 || Hkv < 1 || max_blocks_per_seq < 1 || num_blocks < 1 || max_q_len < 0)
+    return fail(ATTN_ERR_SHAPE, "B, Hq, Hkv, max_blocks_per_seq, num_blocks must be >= 1, max_q_len >= 0");
+  if (Hq % Hkv != 0) return fail(ATTN_ERR_SHAPE, "Hq %d is not a multiple of Hkv %d", Hq, Hkv);
+  if (window < 0) return fail(ATTN_ERR_SHAPE, "window %d < 0", window);
+  if (!(std::isfinite(scale) && scale > 0.f)) return fail(ATTN_ERR_SHAPE, "scale must be finite and > 0");
+  if (!supported_d(D)) return fail(ATTN_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+  if (block_size != 16) return fail(ATTN_ERR_UNSUPPORTED, "block_size %d (supported: 16)", block_size);
+  if ((long long)max_blocks_per_seq * block_size > 0x7fffffffLL)
+    return fail(ATTN_ERR_SHAPE, "max_blocks_per_seq * block_size overflows int32");
+  if (B > 65535) return fail(ATTN_ERR_SHAPE, "B must be <= 65535");
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(ATTN_ERR_NULL, "k_new and v_new must be both given or both NULL");
+  if (total_q == 0 || max_q_len == 0) return ok();
+  if (!q || !k_cache || !v_cache || !block_table || !cu_q || !context_lens || !o)
+    return fail(ATTN_ERR_NULL, "q, k_cache, v_cache, block_table, cu_q, context_lens and o are required");
+  attn::PrefillPagedArgs a{q, k_new, v_new, k_cache, v_cache, block_table, cu_q, context_lens,
+                           o, lse, B, Hq, Hkv, D, max_blocks_per_seq, num_blocks, max_q_len,
+                           total_q, scale, causal != 0, window};
+  attn::launch_prefill_paged(a, reinterpret_cast<hipStream_t>(stream));
+  return check_launch("attn_prefill_paged");
+}
+
 size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_context_len, int window,
                                   int split_tokens) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || max_context_len < 1 || window < 0 ||

@@ -57,6 +57,22 @@ struct AppendArgs {
   int T, Hkv, D, block_size, num_seqs, max_blocks_per_seq, num_blocks;
 };
 
+struct PrefillPagedArgs {
+  const void* q;       // [total_q][Hq][D] packed query rows
+  const void* k_new;   // [total_q][Hkv][D] the chunk's K rows, or null (already in the cache)
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* table;
+  const int32_t* cu_q;  // [B + 1]
+  const int32_t* ctx;   // [B]
+  void* o;
+  float* lse;  // [total_q][Hq] or null
+  int B, Hq, Hkv, D, max_blocks_per_seq, num_blocks, max_q_len, total_q;
+  float scale;
+  int causal, window;
+};
+
 DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int max_context_len, int window,
                        int split_tokens);
 
@@ -64,5 +80,10 @@ int launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 int launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 int launch_decode(const DecodeArgs& a, hipStream_t stream);
 int launch_kv_append(const AppendArgs& a, hipStream_t stream);
+// Append rows of a packed chunk: row r of sequence b (cu_q[b] <= r < cu_q[b+1]) goes to
+// position ctx[b] - (cu_q[b+1] - cu_q[b]) + (r - cu_q[b]). a.seq_idx / a.pos are unused.
+int launch_kv_append_varlen(const AppendArgs& a, const int32_t* cu_q, const int32_t* ctx,
+                            hipStream_t stream);
+int launch_prefill_paged(const PrefillPagedArgs& a, hipStream_t stream);
 
 }  // namespace attn

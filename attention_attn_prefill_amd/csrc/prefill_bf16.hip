@@ -94,12 +94,22 @@ __device__ __forceinline__ int v_swz(int row) {
   return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
 }
 
-template <int D>
+// Paged mode (chunked prefill): queries are packed rows, sequence b owning rows
+// cu_q[b] .. cu_q[b+1]-1, which are the last positions of its ctx[b] keys (bottom-right
+// alignment); K/V come from the paged cache through the block table.
+struct PagedArgs {
+  const int32_t* cu_q;
+  const int32_t* ctx;
+  const int32_t* table;
+  int max_blocks, num_blocks;
+};
+
+template <int D, bool PAGED>
 __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int S,
     int Hq, int Hkv, int G, int HW, int QW, int n_qblk, int n_hsub, float scale_log2,
-    int causal, int window) {
+    int causal, int window, PagedArgs pg) {
   using T = PTile<D>;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
@@ -129,31 +139,40 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(
   const int b = gi / (n_hsub * Hkv);
   const int qblk = causal ? (n_qblk - 1 - qblk_rank) : qblk_rank;
 
+  // Sq query rows at positions off + r against Lk keys (contiguous: Sq = Lk = S, off = 0)
+  int Sq = S, Lk = S, q_row0 = b * S;
+  if constexpr (PAGED) {
+    q_row0 = pg.cu_q[b];
+    Lk = min(max(pg.ctx[b], 0), pg.max_blocks * 16);
+    Sq = min(pg.cu_q[b + 1] - q_row0, Lk);  // rows past the context are not computed
+  }
+  const int off = Lk - Sq;
   const int rows = 32 * QW;
   const int q0 = qblk * rows;
+  if (q0 >= Sq) return;  // whole workgroup: nothing to do for this sequence
   const int head = g * G + hsub * HW + (wave % HW);
   const int q0w = q0 + 32 * (wave / HW);
 
-  // key range of the workgroup and of this wave
-  const int q_last = min(S - 1, q0 + rows - 1);
-  const int kmin = window > 0 ? max(0, q0 - window + 1) : 0;
-  const int kmax = causal ? q_last : S - 1;
+  // key range of the workgroup and of this wave (positions)
+  const int q_last = min(Sq - 1, q0 + rows - 1);
+  const int kmin = window > 0 ? max(0, off + q0 - window + 1) : 0;
+  const int kmax = causal ? off + q_last : Lk - 1;
   const int jlo = kmin / kBN, jhi = kmax / kBN;
-  const bool wave_live = q0w < S;
-  const int qw_last = min(S - 1, q0w + 31);
-  const int kmin_w = window > 0 ? max(0, q0w - window + 1) : 0;
-  const int kmax_w = causal ? qw_last : S - 1;
+  const bool wave_live = q0w < Sq;
+  const int qw_last = min(Sq - 1, q0w + 31);
+  const int kmin_w = window > 0 ? max(0, off + q0w - window + 1) : 0;
+  const int kmax_w = causal ? off + qw_last : Lk - 1;
 
   // ---- Q^T fragments (B operand), kept in registers --------------------------------------
   constexpr int QSTEPS = D / 16;
   bf16x8 qf[QSTEPS];
   {
     const int qr = q0w + col;
-    const uint16_t* qrow = q + (((int64_t)b * S + qr) * Hq + head) * D;
+    const uint16_t* qrow = q + (((int64_t)q_row0 + qr) * Hq + head) * D;
 #pragma unroll
     for (int t = 0; t < QSTEPS; ++t) {
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (qr < S) w = *reinterpret_cast<const u32x4*>(qrow + 16 * t + 8 * half);
+      if (qr < Sq) w = *reinterpret_cast<const u32x4*>(qrow + 16 * t + 8 * half);
       qf[t] = __builtin_bit_cast(bf16x8, w);
     }
   }
@@ -171,28 +190,43 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(
   // this wave issues n = wave + 4i. Lane l fills LDS row r = n*ROWS_PER_INSTR + l / CHUNKS,
   // swizzled chunk l % CHUNKS, i.e. global chunk (l % CHUNKS) ^ swz(r). The swizzles depend on
   // r only through bits that are the same for every i, so each lane has one fixed chunk.
-  const int64_t kv_row_stride = (int64_t)Hkv * D;
-  const uint16_t* kbase = k + ((int64_t)b * S * Hkv + g) * D;
-  const uint16_t* vbase = v + ((int64_t)b * S * Hkv + g) * D;
   const int ld_row0 = wave * T::ROWS_PER_INSTR + lane / T::CHUNKS;
   const int ld_kchunk = (lane % T::CHUNKS) ^ k_swz<D>(ld_row0);
   const int ld_vchunk = (lane % T::CHUNKS) ^ v_swz<D>(ld_row0);
   constexpr int ROW_STEP = 4 * T::ROWS_PER_INSTR;  // rows between this wave's instructions
-
-  // Per-lane element offsets of this wave's rows at k0 = 0; a tile adds k0 * row stride (one
-  // wave-uniform 64-bit product). Only a tile that runs past S clamps rows, to S - 1 (any valid
-  // row will do: keys past S are masked).
+  const int64_t kv_row_stride = (int64_t)Hkv * D;
+  const uint16_t* kbase = k + ((int64_t)b * S * Hkv + g) * D;
+  const uint16_t* vbase = v + ((int64_t)b * S * Hkv + g) * D;
+  // Contiguous: per-lane element offsets of this wave's rows at k0 = 0; a tile adds
+  // k0 * row stride. Paged: one 1 KB load instruction stays inside one 16-key block (16 is a
+  // multiple of the rows per instruction), so its block comes from one wave-uniform table
+  // lookup; the lane adds its slot and chunk.
   int64_t koff[T::PER_WAVE], voff[T::PER_WAVE];
 #pragma unroll
   for (int i = 0; i < T::PER_WAVE; ++i) {
     koff[i] = (int64_t)(ld_row0 + i * ROW_STEP) * kv_row_stride + 8 * ld_kchunk;
     voff[i] = (int64_t)(ld_row0 + i * ROW_STEP) * kv_row_stride + 8 * ld_vchunk;
   }
+  const int pg_slot_k = (ld_row0 & 15) * D + 8 * ld_kchunk;
+  const int pg_slot_v = (ld_row0 & 15) * D + 8 * ld_vchunk;
+  const int pg_blk0 = __builtin_amdgcn_readfirstlane(ld_row0 >> 4);
+  const int pg_nblk = (Lk + 15) >> 4;
   auto issue_tile = [&](int j, int stage) {
     const int k0 = j * kBN;
     char* kdst = smem + stage * T::STAGE + wave * 1024;
     char* vdst = kdst + T::TILE;
-    if (k0 + kBN <= S) {
+    if constexpr (PAGED) {
+      const int32_t* trow = pg.table + (int64_t)b * pg.max_blocks;
+#pragma unroll
+      for (int i = 0; i < T::PER_WAVE; ++i) {
+        const int lb = (k0 >> 4) + pg_blk0 + i * (ROW_STEP >> 4);
+        int pb = lb < pg_nblk ? trow[lb] : 0;  // blocks past the context: any valid block
+        if (pb < 0 || pb >= pg.num_blocks) pb = 0;  // unusable entry: never dereferenced
+        const int64_t boff = ((int64_t)pb * Hkv + g) * 16 * D;
+        lds_dma_16(k + boff + pg_slot_k, lds_addr(kdst + i * 4096));
+        lds_dma_16(v + boff + pg_slot_v, lds_addr(vdst + i * 4096));
+      }
+    } else if (k0 + kBN <= S) {
       const uint16_t* kt = kbase + (int64_t)k0 * kv_row_stride;
       const uint16_t* vt = vbase + (int64_t)k0 * kv_row_stride;
 #pragma unroll
@@ -203,7 +237,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(
     } else {
 #pragma unroll
       for (int i = 0; i < T::PER_WAVE; ++i) {
-        const int row = min(k0 + ld_row0 + i * ROW_STEP, S - 1);
+        const int row = min(k0 + ld_row0 + i * ROW_STEP, S - 1);  // past S: any valid row
         const int64_t roff = (int64_t)row * kv_row_stride;
         lds_dma_16(kbase + roff + 8 * ld_kchunk, lds_addr(kdst + i * 4096));
         lds_dma_16(vbase + roff + 8 * ld_vchunk, lds_addr(vdst + i * 4096));
@@ -253,8 +287,8 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(
     }
     if constexpr (MASK) {
       // register r of block kb holds key offset 32*kb + 8*(r/4) + (r%4) + 4*half of the tile
-      const int qp = q0w + col;
-      int hi = S - 1 - k0;
+      const int qp = off + q0w + col;  // query position
+      int hi = Lk - 1 - k0;
       if (causal) hi = min(hi, qp - k0);
       const int lo_off = window > 0 ? qp - window + 1 - k0 : -(1 << 30);
       const int hi4 = hi - 4 * half, lo4 = lo_off - 4 * half;
@@ -322,8 +356,8 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(
     const bool relevant = wave_live && k0 <= kmax_w && k0 + kBN - 1 >= kmin_w;
     if (relevant) {
       const char* st_base = smem + st * T::STAGE;
-      const bool full = (!causal || k0 + kBN - 1 <= q0w) &&
-                        (window == 0 || qw_last - k0 < window) && (k0 + kBN <= S);
+      const bool full = (!causal || k0 + kBN - 1 <= off + q0w) &&
+                        (window == 0 || off + qw_last - k0 < window) && (k0 + kBN <= Lk);
       if (full)
         tile_step(st_base, k0, std::false_type{});
       else
@@ -333,9 +367,9 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(
 
   // ---- epilogue: O = O^T / l, bf16 RNE ---------------------------------------------------
   const int qr = q0w + col;
-  if (wave_live && qr < S) {
+  if (wave_live && qr < Sq) {
     const float inv = 1.0f / l_run;
-    uint16_t* orow = o + (((int64_t)b * S + qr) * Hq + head) * D;
+    uint16_t* orow = o + (((int64_t)q_row0 + qr) * Hq + head) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -347,38 +381,61 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(
         *reinterpret_cast<u32x2*>(orow + d) = w;
       }
     if (lse != nullptr && half == 0)
-      lse[((int64_t)b * Hq + head) * S + qr] = (m_run + __log2f(l_run)) * kLn2;
+      lse[PAGED ? ((int64_t)q_row0 + qr) * Hq + head : ((int64_t)b * Hq + head) * S + qr] =
+          (m_run + __log2f(l_run)) * kLn2;
   }
 }
 
-template <int D>
-static void launch_d(const PrefillArgs& a, hipStream_t stream) {
-  const int G = a.Hq / a.Hkv;
+template <int D, bool PAGED>
+static void launch_d(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int S, int Hq, int Hkv, float scale, int causal, int window, PagedArgs pg,
+                     hipStream_t stream) {
+  const int G = Hq / Hkv;
   const int HW = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;  // heads per workgroup
   const int QW = 4 / HW;                                    // 32-row chunks per head
   const int rows = 32 * QW;
-  const int n_qblk = (a.S + rows - 1) / rows;
+  const int n_qblk = (S + rows - 1) / rows;  // S: rows per sequence (paged: the largest chunk)
   const int n_hsub = G / HW;
-  const long long nwg = (long long)a.B * a.Hkv * n_hsub * n_qblk;
-  const float scale_log2 = a.scale * kLog2e;
+  const long long nwg = (long long)B * Hkv * n_hsub * n_qblk;
+  const float scale_log2 = scale * kLog2e;
   const size_t lds = 2 * PTile<D>::STAGE;
   static bool attr_set = false;
   if (!attr_set) {
-    hipFuncSetAttribute((const void*)prefill_bf16_kernel<D>,
+    hipFuncSetAttribute((const void*)prefill_bf16_kernel<D, PAGED>,
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr_set = true;
   }
-  hipLaunchKernelGGL(prefill_bf16_kernel<D>, dim3((unsigned)nwg), dim3(kPrefillThreads), lds,
-                     stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (uint16_t*)a.o, a.lse, a.S, a.Hq, a.Hkv, G, HW, QW, n_qblk, n_hsub,
-                     scale_log2, a.causal, a.window);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, PAGED>), dim3((unsigned)nwg), dim3(kPrefillThreads),
+                     lds, stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                     (uint16_t*)o, lse, S, Hq, Hkv, G, HW, QW, n_qblk, n_hsub, scale_log2, causal,
+                     window, pg);
 }
 
 int launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
+  const PagedArgs none{nullptr, nullptr, nullptr, 0, 0};
   if (a.D == 64)
-    launch_d<64>(a, stream);
+    launch_d<64, false>(a.q, a.k, a.v, a.o, a.lse, a.B, a.S, a.Hq, a.Hkv, a.scale, a.causal,
+                        a.window, none, stream);
   else
-    launch_d<128>(a, stream);
+    launch_d<128, false>(a.q, a.k, a.v, a.o, a.lse, a.B, a.S, a.Hq, a.Hkv, a.scale, a.causal,
+                         a.window, none, stream);
+  return 0;
+}
+
+int launch_prefill_paged(const PrefillPagedArgs& a, hipStream_t stream) {
+  if (a.k_new != nullptr) {
+    AppendArgs ap{a.k_new, a.v_new, nullptr, nullptr, a.table, a.k_cache, a.v_cache, nullptr,
+                  nullptr, false, a.total_q, a.Hkv, a.D, 16, a.B, a.max_blocks_per_seq,
+                  a.num_blocks};
+    launch_kv_append_varlen(ap, a.cu_q, a.ctx, stream);
+  }
+  const PagedArgs pg{a.cu_q, a.ctx, a.table, a.max_blocks_per_seq, a.num_blocks};
+  if (a.D == 64)
+    launch_d<64, true>(a.q, a.k_cache, a.v_cache, a.o, a.lse, a.B, a.max_q_len, a.Hq, a.Hkv,
+                       a.scale, a.causal, a.window, pg, stream);
+  else
+    launch_d<128, true>(a.q, a.k_cache, a.v_cache, a.o, a.lse, a.B, a.max_q_len, a.Hq, a.Hkv,
+                        a.scale, a.causal, a.window, pg, stream);
   return 0;
 }
 

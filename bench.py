@@ -32,6 +32,37 @@ import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+COPY_CALIBRATION_BYTES = 256 * 1024 * 1024  # each direction of the calibration copy
+KERNEL_SOURCES = {
+    "prefill_bf16_kernel": "attention_attn_prefill_amd/csrc/prefill_bf16.hip",
+    "decode_split_kernel": "attention_attn_prefill_amd/csrc/decode.hip",
+}
+
+
+def source_hash(kernel: str) -> str:
+    import hashlib
+    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or
+    None when there is none or the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith(" "):
+                k, v = line.split("=", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256_16") != source_hash(kernel):
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def prefill_pairs(S: int, causal: bool, window: int) -> int:
@@ -140,10 +171,12 @@ def main(argv=None):
     ap.add_argument("--workload", default="llama1b", choices=["llama1b", "swa", "int8_70b"])
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0 = skip)")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache-evicting scratch read")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy 3 times (counter calibration)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path is single-GPU; see the sharding notes in the design document)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the attention "
+              "path in this repository runs on a single GPU", file=sys.stderr)
         return 2
 
     import torch as t
@@ -151,6 +184,14 @@ def main(argv=None):
     from synth import WORKLOADS
     A.lib()  # fail loudly if the HIP library is missing
     assert t.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        src = t.ones(COPY_CALIBRATION_BYTES // 4, dtype=t.float32, device="cuda")
+        dst = t.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        t.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": COPY_CALIBRATION_BYTES, "launches": 3}))
+        return 0
 
     pwl = {"llama1b": WORKLOADS["prefill_llama1b_s4096"], "swa": WORKLOADS["prefill_swa_s16384"],
            "int8_70b": None}[args.workload]
@@ -207,7 +248,8 @@ def main(argv=None):
               "workload": f"{dwl.name}: B={dwl.B} Hq={dwl.Hq} Hkv={dwl.Hkv} D={dwl.D} kv={dwl.kv_dtype} "
                           f"ctx=[{dwl.ctx_lo},{dwl.ctx_hi}] window={dwl.window} block=16"}
     roofline_decode = {"bound": "hbm", "achieved": d_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                       "frac": d_gbs / HBM_PEAK_GBS, "traffic": None}
+                       "frac": d_gbs / HBM_PEAK_GBS,
+                       "traffic": measured_traffic("decode_split_kernel", dwl.name)}
     out = {"metric": "paged decode attn HBM GB/s (% peak); prefill attn TFLOP/s (% MFMA peak)",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
@@ -218,7 +260,8 @@ def main(argv=None):
         p_tf = pfl / (p_ms * 1e-3) / 1e12
         out.update(value=p_tf, unit="TFLOP/s")
         out["roofline"] = {"bound": "mfma", "achieved": p_tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": p_tf / BF16_PEAK_TFLOPS, "traffic": None}
+                           "frac": p_tf / BF16_PEAK_TFLOPS,
+                           "traffic": measured_traffic("prefill_bf16_kernel", pwl.name)}
         out["prefill"] = {"kernel": "attn_prefill (bf16 MFMA)", "ms": p_ms, "TFLOP/s": p_tf,
                           "algorithmic_flops": pfl, "tokens_per_s": pwl.B * pwl.S / (p_ms * 1e-3),
                           "workload": f"{pwl.name}: B={pwl.B} S={pwl.S} Hq={pwl.Hq} Hkv={pwl.Hkv} "

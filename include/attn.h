@@ -74,6 +74,36 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, float* ls
                  float scale, int causal, int window, void* stream);
 
 /*
+ * attn_prefill_paged -- chunked (continued) prefill over a paged KV cache, with the chunk's
+ * K/V written into the cache first. [TI] "分页KV缓存：借鉴操作系统的内存管理" (paged cache) and
+ * "Flash Attention：内存与计算的重平衡" (tiled attention with an online softmax); window: [IL].
+ *
+ *  q, o         : [total_q][Hq][D] bf16, packed: sequence b owns rows cu_q[b] .. cu_q[b+1]-1.
+ *  k_new, v_new : [total_q][Hkv][D] bf16, the chunk's keys and values, written (bit copy) to
+ *                 positions context_lens[b] - q_len_b .. context_lens[b] - 1 of sequence b
+ *                 (q_len_b = cu_q[b+1] - cu_q[b]) before attention runs; both NULL when the
+ *                 cache already holds them.
+ *  k_cache,
+ *  v_cache      : bf16 [num_blocks][Hkv][block_size][D], block_table int32
+ *                 [B][max_blocks_per_seq], as in attn_decode_paged.
+ *  cu_q         : int32 [B + 1], cu_q[0] = 0, non-decreasing, cu_q[B] = total_q.
+ *  context_lens : int32 [B], keys of each sequence after the chunk (q_len_b <= context_lens[b]
+ *                 <= max_blocks_per_seq * block_size); row i of sequence b sits at position
+ *                 context_lens[b] - q_len_b + i (bottom-right alignment).
+ *  lse          : optional fp32 [total_q][Hq] (natural-log log-sum-exp), or NULL.
+ *  max_q_len    : host-side bound on every q_len_b, used to size the grid.
+ *  Requirements: D in {64, 128}; block_size == 16; Hq % Hkv == 0; total_q >= 0 (0 is a no-op);
+ *  causal and window as in attn_prefill; bf16 only. Rows whose chunk is longer than the context
+ *  are left unwritten; table entries outside [0, num_blocks) are never dereferenced.
+ */
+int attn_prefill_paged(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                       void* v_cache, const int32_t* block_table, const int32_t* cu_q,
+                       const int32_t* context_lens, void* o, float* lse, int B, int Hq, int Hkv,
+                       int D, int block_size, int max_blocks_per_seq, int num_blocks,
+                       int max_q_len, int total_q, float scale, int causal, int window,
+                       void* stream);
+
+/*
  * attn_decode_workspace_size -- bytes of device workspace attn_decode_paged needs for these
  * sizes (0 when the call runs as a single pass and needs none). split_tokens as below.
  */

@@ -38,7 +38,7 @@ import numpy as np
 
 __all__ = [
     "visible_mask", "attention_head", "attention", "gather_logical", "decode_paged",
-    "quantize_int8", "dequantize_int8", "append_expected", "merge_partials",
+    "prefill_paged", "quantize_int8", "dequantize_int8", "append_expected", "merge_partials",
 ]
 
 
@@ -157,6 +157,34 @@ def decode_paged(q, k_pool, v_pool, table, ctx, scale: float, block_size: int, w
             ob, lb = attention_head(q[b, h][None, :], kk[:, g, :], vv[:, g, :], scale,
                                     [n - 1], True, window)
             o[b, h], lse[b, h] = ob[0], lb[0]
+    return o, lse
+
+
+def prefill_paged(q, cu_q, k_pool, v_pool, table, ctx, scale: float, block_size: int,
+                  causal: bool = True, window: int = 0):
+    """Chunked prefill against a paged cache that already holds every key of the chunk.
+
+    q: [total_q][Hq][D] packed rows; sequence b owns rows cu_q[b] .. cu_q[b+1]-1, the last
+    q_len_b = cu_q[b+1] - cu_q[b] positions of its ctx[b] keys, so row i of b sits at position
+    ctx[b] - q_len_b + i (bottom-right alignment). Pools [num_blocks][Hkv][bs][D].
+    Returns (o [total_q][Hq][D], lse [total_q][Hq]).
+    """
+    total, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    G = Hq // Hkv
+    o = np.zeros((total, Hq, v_pool.shape[3]))
+    lse = np.zeros((total, Hq))
+    for b in range(len(ctx)):
+        r0, r1 = int(cu_q[b]), int(cu_q[b + 1])
+        if r1 == r0:
+            continue
+        n = int(ctx[b])
+        kk = gather_logical(k_pool, table[b], n, block_size)
+        vv = gather_logical(v_pool, table[b], n, block_size)
+        qpos = np.arange(r1 - r0) + (n - (r1 - r0))
+        for h in range(Hq):
+            o[r0:r1, h], lse[r0:r1, h] = attention_head(q[r0:r1, h], kk[:, h // G], vv[:, h // G],
+                                                        scale, qpos, causal, window)
     return o, lse
 
 

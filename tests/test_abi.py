@@ -116,3 +116,23 @@ def _append(**kw):
 ])
 def test_append_validation(kw, code):
     assert _append(**kw) == code
+
+
+def _paged(**kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, table=FAKE, cu=FAKE, ctx=FAKE, o=FAKE, lse=None,
+             B=2, Hq=8, Hkv=2, D=64, bs=16, mb=4, nb=8, mq=16, tq=20, scale=0.125, causal=1, window=0)
+    a.update(kw)
+    return A.lib().attn_prefill_paged(a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["table"], a["cu"],
+                                      a["ctx"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"],
+                                      a["mb"], a["nb"], a["mq"], a["tq"], a["scale"], a["causal"],
+                                      a["window"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), A.ATTN_ERR_NULL), (dict(cu=None), A.ATTN_ERR_NULL), (dict(kn=None), A.ATTN_ERR_NULL),
+    (dict(tq=-1), A.ATTN_ERR_SHAPE), (dict(Hq=6, Hkv=4), A.ATTN_ERR_SHAPE), (dict(window=-1), A.ATTN_ERR_SHAPE),
+    (dict(scale=-1.0), A.ATTN_ERR_SHAPE), (dict(D=96), A.ATTN_ERR_UNSUPPORTED), (dict(bs=32), A.ATTN_ERR_UNSUPPORTED),
+    (dict(tq=0, q=None), A.ATTN_OK),
+])
+def test_prefill_paged_validation(kw, code):
+    assert _paged(**kw) == code

@@ -425,3 +425,52 @@ def test_golden_regression():
     now = compute()
     for key, val in stored.items():
         assert np.abs(np.asarray(val) - np.asarray(now[key])).max() < 1e-12, key
+
+
+# --- chunked prefill over the paged cache ---------------------------------------------------------
+def _scatter(pool, table, rows_per_seq, bs):
+    """Test-side placement of logical rows into a pool (independent of the oracle)."""
+    for b, rows in enumerate(rows_per_seq):
+        for t in range(len(rows)):
+            pool[table[b][t // bs], :, t % bs] = rows[t]
+
+
+@pytest.mark.parametrize("window", [0, 3, 50])
+def test_prefill_paged_chunks_equal_full_prefill(window):
+    """Each chunk of a sequence's queries against its paged prefix equals the full prefill rows."""
+    rng = np.random.default_rng(31 + window)
+    bs, Hq, Hkv, D = 4, 4, 2, 8
+    S = np.array([13, 6, 20])
+    table, nb = paged_table(S, bs, 9, 2, True)
+    q = [rng.standard_normal((n, Hq, D)) for n in S]
+    k = [rng.standard_normal((n, Hkv, D)) for n in S]
+    v = [rng.standard_normal((n, Hkv, D)) for n in S]
+    kp, vp = np.full((nb, Hkv, bs, D), np.nan), np.full((nb, Hkv, bs, D), np.nan)
+    _scatter(kp, table, k, bs)
+    _scatter(vp, table, v, bs)
+    full = [oracle.attention(q[b][None], k[b][None], v[b][None], 0.4, True, window)[0][0] for b in range(3)]
+    # three chunk rounds with ragged chunk sizes (0 allowed)
+    cuts = [np.array([0, 5, 13]), np.array([0, 1, 6]), np.array([7, 20, 20])]
+    done = np.zeros(3, int)
+    for r in range(3):
+        new = [min(int(cuts[r][b]), int(S[b])) - done[b] if r < 2 else int(S[b]) - done[b] for b in range(3)]
+        new = [max(0, x) for x in new]
+        ctx = done + np.array(new)
+        cu = np.concatenate([[0], np.cumsum(new)])
+        qc = np.concatenate([q[b][done[b]:ctx[b]] for b in range(3)])
+        o, _ = oracle.prefill_paged(qc, cu, kp, vp, table, ctx, 0.4, bs, True, window)
+        for b in range(3):
+            assert np.abs(o[cu[b]:cu[b + 1]] - full[b][done[b]:ctx[b]]).max(initial=0) < 1e-13
+        done = ctx
+
+
+def test_prefill_paged_single_row_is_decode():
+    rng = np.random.default_rng(77)
+    bs = 3
+    ctx = np.array([7, 1, 11], np.int32)
+    table, nb = paged_table(ctx, bs, 5, 1, True)
+    kp, vp = rng.standard_normal((nb, 2, bs, 4)), rng.standard_normal((nb, 2, bs, 4))
+    q = rng.standard_normal((3, 4, 4))
+    od, _ = oracle.decode_paged(q, kp, vp, table, ctx, 0.3, bs, 2)
+    op, _ = oracle.prefill_paged(q, np.arange(4), kp, vp, table, ctx, 0.3, bs, True, 2)
+    assert np.abs(od - op).max() < 1e-14
