@@ -11,6 +11,8 @@ Each call is bracketed by HIP events on the stream the library launches on. The 
 `value` is the prefill TFLOP/s (algorithmic flops: visible (query, key) pairs x 4D) over the
 timed steps; the decode HBM GB/s (algorithmic bytes: each visible K/V byte once, plus Q and O)
 is reported beside it. `--workload swa` / `int8_70b` time the other configurations the same way.
+Outside the timed steps, the default run also times attn_prefill_paged (chunked prefill over
+the paged cache with fused append: 4 sequences, 1024-token chunks after 3072-token prefixes).
 
 Prints one JSON line. Inputs are seeded synthetic tensors (synth/) resident in HBM before the
 timed region starts.
@@ -137,6 +139,62 @@ def setup_decode(t, wl):
     return d
 
 
+CHUNK = dict(B=4, ctx=4096, q_len=1024, Hq=32, Hkv=8, D=64, seed=1202)
+
+
+def setup_chunked(t):
+    """Chunked prefill over the paged cache (Llama-3.2-1B heads): 4 sequences whose 3072-token
+    prefixes sit in a permuted bf16 pool; each call appends and attends a 1024-token chunk."""
+    from synth import DecodeWorkload, new_tokens, paged_table, pool
+    c = CHUNK
+    ctx = np.full(c["B"], c["ctx"], np.int32)
+    wl = DecodeWorkload("chunk_llama1b", c["seed"], "bf16", c["B"], c["Hq"], c["Hkv"], c["D"], c["ctx"], c["ctx"])
+    table, nb = paged_table(ctx, 16, c["seed"])
+    T = c["B"] * c["q_len"]
+    kn, _ = new_tokens(c["seed"] + 1, T, c["Hkv"], c["D"], "k")
+    vn, _ = new_tokens(c["seed"] + 2, T, c["Hkv"], c["D"], "v")
+    qb, _ = new_tokens(c["seed"] + 3, T, c["Hq"], c["D"], "k")
+    cu = np.arange(c["B"] + 1, dtype=np.int32) * c["q_len"]
+    return dict(q=_bf16(t, qb), kn=_bf16(t, kn), vn=_bf16(t, vn), kc=_bf16(t, pool(wl, "k", nb)),
+                vc=_bf16(t, pool(wl, "v", nb)), table=t.from_numpy(table).cuda(),
+                cu=t.from_numpy(cu).cuda(), ctx=t.from_numpy(ctx).cuda(),
+                o=t.empty((T, c["Hq"], c["D"]), dtype=t.bfloat16, device="cuda"))
+
+
+def chunked_flops() -> float:
+    c = CHUNK
+    prefix = c["ctx"] - c["q_len"]
+    pairs = c["q_len"] * prefix + c["q_len"] * (c["q_len"] + 1) // 2
+    return 4.0 * c["D"] * c["Hq"] * c["B"] * pairs
+
+
+def time_chunked(t, A, reps: int):
+    """attn_prefill_paged with fused append, timed per call with events (outside the step)."""
+    C = setup_chunked(t)
+    c = CHUNK
+
+    def call():
+        A.attn_prefill_paged(C["q"], C["kc"], C["vc"], C["table"], C["cu"], C["ctx"], c["q_len"],
+                             k_new=C["kn"], v_new=C["vn"], causal=True, out=C["o"])
+    for _ in range(3):
+        call()
+    ev = [(t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        call()
+        e1.record()
+    t.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    fl = chunked_flops()
+    tf = fl / (ms * 1e-3) / 1e12
+    return {"kernel": "attn_prefill_paged (varlen append + paged bf16 MFMA prefill)", "ms": ms,
+            "TFLOP/s": tf, "frac_mfma_peak": tf / BF16_PEAK_TFLOPS, "algorithmic_flops": fl,
+            "tokens_per_s": c["B"] * c["q_len"] / (ms * 1e-3), "calls": reps,
+            "workload": f"B={c['B']} chunks of {c['q_len']} rows after {c['ctx'] - c['q_len']}-token "
+                        f"prefixes, Hq={c['Hq']} Hkv={c['Hkv']} D={c['D']} causal, block 16, "
+                        "permuted pool"}
+
+
 def cpu_baseline(pwl, dwl, budget_s: float):
     """The oracle, untuned, on a time-bounded sample of the same workload."""
     import oracle
@@ -171,6 +229,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="llama1b", choices=["llama1b", "swa", "int8_70b"])
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0 = skip)")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache-evicting scratch read")
+    ap.add_argument("--no-chunked", action="store_true",
+                    help="skip the chunked paged prefill timing reported beside the step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 3 times (counter calibration)")
     args = ap.parse_args(argv)
@@ -273,6 +333,8 @@ def main(argv=None):
     out["roofline_decode"] = roofline_decode
     out["config"] = {"workload": (f"{pwl.name} + {dwl.name}" if pwl else dwl.name),
                      "step": "kv_cache_append -> cache flush -> attn_decode_paged -> attn_prefill"}
+    if args.workload == "llama1b" and not args.no_chunked:
+        out["prefill_paged"] = time_chunked(t, A, max(5, args.steps))
     if args.cpu_budget > 0 and pwl is not None:
         out["cpu_baseline"] = cpu_baseline(pwl, dwl, args.cpu_budget)
     print(json.dumps(out), flush=True)
