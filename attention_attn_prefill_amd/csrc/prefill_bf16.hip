@@ -273,18 +273,20 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(
   // edge or the ragged end of the sequence); interior tiles skip all mask arithmetic.
   auto tile_step = [&](const char* st_base, int k0, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    // S^T = K Q^T
+    // S^T = K Q^T; the two 32-key blocks alternate so consecutive MFMAs are independent
+    // (a dependent accumulation chain would wait for each result)
     f32x16 sacc[kBN / 32];
 #pragma unroll
-    for (int kb = 0; kb < kBN / 32; ++kb) {
+    for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
 #pragma unroll
-      for (int t = 0; t < QSTEPS; ++t) {
+    for (int t = 0; t < QSTEPS; ++t)
+#pragma unroll
+      for (int kb = 0; kb < kBN / 32; ++kb) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(st_base + kaddr_t[t] + kb * 32 * T::ROWB);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], sacc[kb], 0, 0, 0);
       }
-    }
     if constexpr (MASK) {
       // register r of block kb holds key offset 32*kb + 8*(r/4) + (r%4) + 4*half of the tile
       const int qp = off + q0w + col;  // query position
