@@ -9,10 +9,15 @@
 // ("Triton融合算子优化：LLM推理性能提升3倍的工程实践") -- "一、LLM推理的算子瓶颈" (decode is bound by
 // reading the KV cache from memory).
 //
-// Design (gfx950): one workgroup of 4 waves per (split, KV head g, sequence b). A split is a
-// run of `C` consecutive logical tokens, block aligned. All G = Hq/Hkv query heads of g are
-// served by the same workgroup, so every K/V byte is read from HBM once.
-// Each wave walks the split in chunks of U blocks; for a chunk it
+// Design (gfx950). All G = Hq/Hkv query heads of a KV head g are served by the same wave, so
+// every K/V byte is read from HBM once. The work is the list of (sequence b, KV head g,
+// 16-token block) triples that hold visible tokens; two launch shapes split it:
+//  * balanced (the default): a persistent grid whose waves each take an equal contiguous range
+//    of that list, so ragged context lengths cost no imbalance; a wave writes one partial per
+//    (b, g) segment its range touches, or the final output when it holds a whole segment;
+//  * fixed split (split_tokens > 0): one workgroup of 4 waves per (split of C tokens, g, b),
+//    the waves merged in LDS.
+// A wave walks its blocks in chunks of U blocks; for a chunk it
 //   * issues the table lookups and every K and V load of the chunk at once (deep memory-level
 //     parallelism: 16-32 KB in flight per wave),
 //   * computes QK^T on MFMA 16x16x32: A = 16 tokens of a K block in their natural [token][d]
@@ -23,8 +28,7 @@
 //   * hands the probabilities to the PV lanes through a small per-wave LDS slice and does PV on
 //     the VALU, each lane owning 8 consecutive d of one token (coalesced V rows); the INT8 V
 //     scale is folded into the probability.
-// The 4 waves' (m, l, acc) are merged by log-sum-exp in LDS; the workgroup then writes the
-// bf16 output (single split) or an fp32 partial (o, lse) merged by decode_merge_kernel.
+// Partials (o, lse) are merged by log-sum-exp in a second small kernel.
 #include "common.h"
 #include "launch.h"
 #include <hip/hip_fp16.h>
@@ -84,6 +88,303 @@ struct DecodeShape {
   static constexpr int VLOADS = BS / TPW;                  // V loads per lane per block
 };
 
+// Per-wave decode state: Q fragments, running max, row-sum shares and PV accumulators of the
+// G heads of one (sequence, KV head). The LDS staging slices belong to the wave.
+template <int D, int GP, bool I8>
+struct DecodeWave {
+  using SH = DecodeShape<D, I8>;
+  static constexpr int BS = SH::BS, U = SH::U, CT = U * BS;  // CT tokens per chunk
+  typedef typename std::conditional<I8, f16x8, bf16x8>::type frag_t;
+  typedef typename std::conditional<I8, u32x2, u32x4>::type vword_t;
+  // probabilities handed from the MFMA lanes to the PV lanes: fp32 [token][head] for bf16;
+  // for INT8, fp16 pairs (token t, token t + 8) of p' = p * v_scale, [block][pair][head]
+  struct Lds {
+    float p[I8 ? 1 : CT][GP];
+    uint32_t pp[I8 ? U : 1][8][GP];
+    float alpha[GP];
+  };
+
+  int lane, hq, grp, c8, ts;
+  frag_t qf[SH::KSTEPS];
+  float bias;     // INT8: 1152 * sum of this head's fp16 q values (the widened codes carry +1152)
+  float m_run;    // per head (lanes hq), log2 units
+  float l_part;   // this lane's share of the row sum
+  float ps_part;  // INT8: this lane's share of sum(p'), in the fp16 values used
+  float acc[GP][8];
+
+  __device__ __forceinline__ void init(int lane_) {
+    lane = lane_;
+    hq = lane & 15;  // MFMA (QK^T) lane roles: column = query head, rows = 4 tokens of a block
+    grp = lane >> 4;
+    c8 = lane % SH::CPR;  // PV lane roles: 8 consecutive d of one token (bf16) or a token pair (INT8)
+    ts = lane / SH::CPR;
+  }
+
+  // Q^T of heads g*G .. g*G+G-1 (qrow: head g*G of the sequence), padded to 16 columns
+  __device__ __forceinline__ void load_q(const uint16_t* __restrict__ qrow, int G) {
+    float qsum = 0.f;
+    qrow += (int64_t)hq * D;
+#pragma unroll
+    for (int j = 0; j < SH::KSTEPS; ++j) {
+      // bf16: step j covers d = 32j + 8*grp + e; INT8: one 16-byte load feeds steps 2jj,
+      // 2jj+1 covering d = 64*jj + 16*grp + 8*sub + e.
+      const int d0 = I8 ? (64 * (j / 2) + 16 * grp + 8 * (j % 2)) : (32 * j + 8 * grp);
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (hq < G) w = *reinterpret_cast<const u32x4*>(qrow + d0);
+      if constexpr (I8) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qf[j][2 * e] = (_Float16)bf16_lo(w[e]);
+          qf[j][2 * e + 1] = (_Float16)bf16_hi(w[e]);
+          qsum += (float)qf[j][2 * e] + (float)qf[j][2 * e + 1];
+        }
+      } else {
+        qf[j] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+    if constexpr (I8) {
+      qsum += __shfl_xor(qsum, 16);
+      qsum = sum_x32(qsum);
+    }
+    bias = kI8Bias * qsum;
+  }
+
+  __device__ __forceinline__ void reset() {
+    m_run = kNegBig;
+    l_part = 0.f;
+    ps_part = 0.f;
+#pragma unroll
+    for (int h = 0; h < GP; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  }
+
+  // The registers of one chunk in flight: blocks pb[u] (physical; okb[u] false = skip)
+  // holding logical tokens t0 + 16u .. t0 + 16u + 15.
+  struct Chunk {
+    u32x4 kw[U][SH::KLOADS];
+    vword_t vw[U][SH::VLOADS];
+    float ksc[U][4], vsc[U][4];
+    int pb[U];
+    bool okb[U];
+    int t0;
+  };
+
+  // Issue every load of a chunk (pb, okb and t0 already set).
+  __device__ __forceinline__ void load(Chunk& c, const void* __restrict__ k_cache,
+                                       const void* __restrict__ v_cache,
+                                       const __half* __restrict__ k_scale,
+                                       const __half* __restrict__ v_scale, int Hkv, int g) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t brow = pool_offset(c.pb[u], Hkv, g, BS, 0, D);
+      if constexpr (I8) {
+        const int8_t* kc = reinterpret_cast<const int8_t*>(k_cache) + brow + (int64_t)hq * D;
+#pragma unroll
+        for (int jj = 0; jj < SH::KLOADS; ++jj)
+          c.kw[u][jj] = ld_stream<u32x4>(kc + 64 * jj + 16 * grp);
+        const int8_t* vc = reinterpret_cast<const int8_t*>(v_cache) + brow;
+#pragma unroll
+        for (int i = 0; i < SH::VLOADS; ++i)
+          c.vw[u][i] = ld_stream<u32x2>(vc + (int64_t)(i * SH::TPW + ts) * D + 8 * c8);
+        const int64_t srow = ((int64_t)c.pb[u] * Hkv + g) * BS + 4 * grp;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          c.ksc[u][i] = __half2float(k_scale[srow + i]);
+          c.vsc[u][i] = __half2float(v_scale[srow + i]);
+        }
+      } else {
+        const uint16_t* kc = reinterpret_cast<const uint16_t*>(k_cache) + brow + (int64_t)hq * D;
+#pragma unroll
+        for (int j = 0; j < SH::KLOADS; ++j)
+          c.kw[u][j] = ld_stream<u32x4>(kc + 32 * j + 8 * grp);
+        const uint16_t* vc = reinterpret_cast<const uint16_t*>(v_cache) + brow;
+#pragma unroll
+        for (int i = 0; i < SH::VLOADS; ++i)
+          c.vw[u][i] = ld_stream<u32x4>(vc + (int64_t)(i * SH::TPW + ts) * D + 8 * c8);
+      }
+    }
+  }
+
+  // Online softmax + PV of a loaded chunk; tokens outside [lo, hi) are masked.
+  __device__ __forceinline__ void compute(const Chunk& c, int lo, int hi, float scale_log2,
+                                          Lds& L) {
+    // ---- scores on MFMA -----------------------------------------------------------------
+    float sc[U][4];
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (I8) {
+#pragma unroll
+        for (int jj = 0; jj < SH::KLOADS; ++jj)
+#pragma unroll
+          for (int sub = 0; sub < 2; ++sub) {
+            const uint32_t w0 = c.kw[u][jj][2 * sub] ^ 0x80808080u;
+            const uint32_t w1 = c.kw[u][jj][2 * sub + 1] ^ 0x80808080u;
+            const u32x4 hv = {widen_lo(w0), widen_hi(w0), widen_lo(w1), widen_hi(w1)};
+            a4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, hv),
+                                                        qf[2 * jj + sub], a4, 0, 0, 0);
+          }
+      } else {
+#pragma unroll
+        for (int j = 0; j < SH::KSTEPS; ++j)
+          a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, c.kw[u][j]), qf[j], a4, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = c.t0 + u * BS + 4 * grp + i;
+        const bool vis = c.okb[u] && t >= lo && t < hi;
+        float s;
+        if constexpr (I8)
+          s = (a4[i] - bias) * c.ksc[u][i] * scale_log2;
+        else
+          s = a4[i] * scale_log2;
+        sc[u][i] = vis ? s : -INFINITY;
+        cmax = fmaxf(cmax, sc[u][i]);
+      }
+    }
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+    cmax = max_x32(cmax);
+    // lazy rescale: move the running max only when it grows by more than 8 (log2 units)
+    if (__builtin_amdgcn_ballot_w64(cmax > m_run + 8.0f) != 0) {
+      const float m_new = fmaxf(m_run, cmax);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_part *= alpha;
+      ps_part *= alpha;
+      if (grp == 0 && hq < GP) L.alpha[hq] = alpha;
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int h = 0; h < GP; ++h) {
+        const float al = L.alpha[h];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= al;
+      }
+    }
+    // probabilities -> LDS
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = fast_exp2(sc[u][i] - m_run);
+        l_part += p;
+        if constexpr (I8) {
+          // masked tokens: p = 0 exactly, and their (possibly NaN) scale is not used
+          const _Float16 pv16 = (_Float16)(sc[u][i] == -INFINITY ? 0.f : p * c.vsc[u][i]);
+          ps_part += (float)pv16;
+          const int t = 4 * grp + i;  // token inside block u: pair t & 7, element t >> 3
+          if (hq < GP) reinterpret_cast<_Float16*>(&L.pp[u][t & 7][hq])[t >> 3] = pv16;
+        } else {
+          if (hq < GP) L.p[u * BS + 4 * grp + i][hq] = p;
+        }
+      }
+    __builtin_amdgcn_wave_barrier();
+    // ---- PV on the VALU -------------------------------------------------------------------
+    if constexpr (I8) {
+      // lane (ts, c8) owns tokens ts + TPW*i of each block; it pairs t = ts + TPW*pr with t + 8
+      // and accumulates p'_t (1152 + x_t[d]) with v_dot2_f32_f16 (codes are finite, masked
+      // tokens have p' = 0)
+      constexpr int NPAIR = SH::VLOADS / 2;
+      static_assert(SH::TPW * NPAIR == 8, "token pairs are (t, t + 8)");
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int pr = 0; pr < NPAIR; ++pr) {
+          const int pair = ts + SH::TPW * pr;
+          const u32x2 bw = c.vw[u][pr], cw = c.vw[u][pr + NPAIR];
+          uint32_t xp[8];  // fp16 pairs (1152 + x_t, 1152 + x_{t+8}) for the lane's 8 d
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const uint32_t bx = bw[k] ^ 0x80808080u, cx = cw[k] ^ 0x80808080u;
+            const uint32_t i0 = __builtin_amdgcn_perm(cx, bx, 0x05010400u);  // b0 c0 b1 c1
+            const uint32_t i1 = __builtin_amdgcn_perm(cx, bx, 0x07030602u);  // b2 c2 b3 c3
+            xp[4 * k + 0] = widen_lo(i0);
+            xp[4 * k + 1] = widen_hi(i0);
+            xp[4 * k + 2] = widen_lo(i1);
+            xp[4 * k + 3] = widen_hi(i1);
+          }
+          uint32_t pp[GP];
+#pragma unroll
+          for (int h4 = 0; h4 < GP; h4 += 4) {
+            if constexpr (GP >= 4) {
+              const u32x4 p4 = *reinterpret_cast<const u32x4*>(&L.pp[u][pair][h4]);
+              pp[h4] = p4[0]; pp[h4 + 1] = p4[1]; pp[h4 + 2] = p4[2]; pp[h4 + 3] = p4[3];
+            } else {
+#pragma unroll
+              for (int h = 0; h < GP; ++h) pp[h] = L.pp[u][pair][h];
+            }
+          }
+#pragma unroll
+          for (int h = 0; h < GP; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              acc[h][e] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pp[h]),
+                                                 __builtin_bit_cast(f16x2, xp[e]), acc[h][e], false);
+        }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < SH::VLOADS; ++i) {
+          const int slot = i * SH::TPW + ts;
+          const int tpos = c.t0 + u * BS + slot;
+          if (!(c.okb[u] && tpos >= lo && tpos < hi)) continue;  // masked slot may hold NaN
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[2 * e] = bf16_lo(c.vw[u][i][e]);
+            x[2 * e + 1] = bf16_hi(c.vw[u][i][e]);
+          }
+          float pv[GP];
+#pragma unroll
+          for (int h4 = 0; h4 < GP; h4 += 4) {
+            if constexpr (GP >= 4) {
+              const f32x4 p4 = *reinterpret_cast<const f32x4*>(&L.p[u * BS + slot][h4]);
+              pv[h4] = p4[0]; pv[h4 + 1] = p4[1]; pv[h4 + 2] = p4[2]; pv[h4 + 3] = p4[3];
+            } else {
+#pragma unroll
+              for (int h = 0; h < GP; ++h) pv[h] = L.p[u * BS + slot][h];
+            }
+          }
+#pragma unroll
+          for (int h = 0; h < GP; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pv[h], x[e], acc[h][e]);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();  // the staging slices are rewritten by the next chunk
+  }
+
+  // Reduce inside the wave: returns this head's row sum l and sum(p') (lanes hq); afterwards
+  // the lanes with ts == 0 hold the complete accumulators of d = 8*c8 .. 8*c8+7, with the
+  // INT8 bias already removed.
+  __device__ __forceinline__ void reduce(float& l_w, float& ps_w) {
+    l_w = l_part + __shfl_xor(l_part, 16);  // lanes hq, hq+16, hq+32, hq+48
+    l_w = sum_x32(l_w);
+    ps_w = 0.f;
+    if constexpr (I8) {
+      ps_w = ps_part + __shfl_xor(ps_part, 16);
+      ps_w = sum_x32(ps_w);
+    }
+#pragma unroll
+    for (int h = 0; h < GP; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int o = SH::CPR; o < 64; o <<= 1) acc[h][e] += __shfl_xor(acc[h][e], o);
+    if constexpr (I8) {
+#pragma unroll
+      for (int h = 0; h < GP; ++h) {
+        const float corr = kI8Bias * __shfl(ps_w, h);  // remove the +1152 of the codes
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] -= corr;
+      }
+    }
+  }
+};
+
+// ---- fixed split: one workgroup of 4 waves per (split, g, b) --------------------------------
 template <int D, int GP, bool I8>
 __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ k_cache,
@@ -93,15 +394,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     float* __restrict__ part_o, float* __restrict__ part_lse, int Hq, int Hkv, int G,
     int max_blocks, int num_blocks, int max_ctx, float scale_log2, int window, int C,
     int n_split) {
-  using SH = DecodeShape<D, I8>;
-  constexpr int BS = SH::BS, U = SH::U, CT = U * BS;  // CT tokens per chunk
-  // probabilities handed from the MFMA lanes to the PV lanes: fp32 [token][head] for bf16;
-  // for INT8, fp16 pairs (token t, token t + 8) of p' = p * v_scale, [block][pair][head]
-  __shared__ float s_p[kDecodeWaves][I8 ? 1 : CT][GP];
-  __shared__ uint32_t s_pp[kDecodeWaves][I8 ? U : 1][8][GP];
-  __shared__ float s_alpha[kDecodeWaves][GP];
+  using W = DecodeWave<D, GP, I8>;
+  constexpr int BS = W::BS, U = W::U;
+  __shared__ typename W::Lds s_lds[kDecodeWaves];
   __shared__ float s_red[kDecodeWaves][GP][D];
-  __shared__ float s_ml[kDecodeWaves][3][GP];
+  __shared__ float s_ml[kDecodeWaves][2][GP];
   __shared__ int s_pb[kMaxSplitBlocks];  // the split's slice of the block table
 
   // Grid (Hkv, B, n_split) with the split index slowest and reversed: consecutive workgroups
@@ -135,273 +432,41 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
   }
   __syncthreads();
 
-  // MFMA (QK^T) lane roles: column = query head, rows = 4 tokens of the block
-  const int hq = lane & 15, grp = lane >> 4;
-  // PV lane roles: 8 consecutive d of one token (bf16) or of a token pair (INT8)
-  const int c8 = lane % SH::CPR, ts = lane / SH::CPR;
-
-  typedef typename std::conditional<I8, f16x8, bf16x8>::type frag_t;
-  frag_t qf[SH::KSTEPS];
-  float qsum = 0.f;  // INT8: sum of this head's fp16 q values (the widened codes carry +1152)
-  {
-    const uint16_t* qrow = q + ((int64_t)b * Hq + g * G + hq) * D;
-#pragma unroll
-    for (int j = 0; j < SH::KSTEPS; ++j) {
-      // bf16: step j covers d = 32j + 8*grp + e; INT8: one 16-byte load feeds steps 2jj,
-      // 2jj+1 covering d = 64*jj + 16*grp + 8*sub + e.
-      const int d0 = I8 ? (64 * (j / 2) + 16 * grp + 8 * (j % 2)) : (32 * j + 8 * grp);
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (hq < G) w = *reinterpret_cast<const u32x4*>(qrow + d0);
-      if constexpr (I8) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          qf[j][2 * e] = (_Float16)bf16_lo(w[e]);
-          qf[j][2 * e + 1] = (_Float16)bf16_hi(w[e]);
-          qsum += (float)qf[j][2 * e] + (float)qf[j][2 * e + 1];
-        }
-      } else {
-        qf[j] = __builtin_bit_cast(bf16x8, w);
-      }
-    }
-    if constexpr (I8) {
-      qsum += __shfl_xor(qsum, 16);
-      qsum = sum_x32(qsum);
-    }
-  }
-  const float bias = kI8Bias * qsum;
-
-  float m_run = kNegBig;  // per head (lanes hq), log2 units
-  float l_part = 0.f;     // this lane's share of the row sum
-  float ps_part = 0.f;    // INT8: this lane's share of sum(p'), in the fp16 values used
-  float acc[GP][8];
-#pragma unroll
-  for (int h = 0; h < GP; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-
+  W w;
+  w.init(lane);
+  w.load_q(q + ((int64_t)b * Hq + g * G) * D, G);
+  w.reset();
+  // this wave's chunks are ch = wave, wave + 4, ...
   const int nchunk = (nblk + U - 1) / U;
-  for (int ch = wave; ch < nchunk; ch += kDecodeWaves) {
+  typename W::Chunk cA;
+  auto prep = [&](typename W::Chunk& c, int ch) {
     const int blk0 = ch * U;
-    int pb[U];
-    bool okb[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int blk = blk0 + u;
-      pb[u] = __builtin_amdgcn_readfirstlane(blk < nblk ? s_pb[blk] : -1);
-      okb[u] = pb[u] >= 0;
-      if (!okb[u]) pb[u] = 0;
+      const int e = __builtin_amdgcn_readfirstlane(blk < nblk ? s_pb[blk] : -1);
+      c.okb[u] = e >= 0;
+      c.pb[u] = c.okb[u] ? e : 0;
     }
-    // ---- issue every load of the chunk -------------------------------------------------
-    u32x4 kw[U][SH::KLOADS];
-    typedef typename std::conditional<I8, u32x2, u32x4>::type vword_t;
-    vword_t vw[U][SH::VLOADS];
-    float ksc[U][4], vsc[U][4];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t brow = pool_offset(pb[u], Hkv, g, BS, 0, D);
-      if constexpr (I8) {
-        const int8_t* kc = reinterpret_cast<const int8_t*>(k_cache) + brow + (int64_t)hq * D;
-#pragma unroll
-        for (int jj = 0; jj < SH::KLOADS; ++jj)
-          kw[u][jj] = ld_stream<u32x4>(kc + 64 * jj + 16 * grp);
-        const int8_t* vc = reinterpret_cast<const int8_t*>(v_cache) + brow;
-#pragma unroll
-        for (int i = 0; i < SH::VLOADS; ++i)
-          vw[u][i] = ld_stream<u32x2>(vc + (int64_t)(i * SH::TPW + ts) * D + 8 * c8);
-        const int64_t srow = ((int64_t)pb[u] * Hkv + g) * BS + 4 * grp;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ksc[u][i] = __half2float(k_scale[srow + i]);
-          vsc[u][i] = __half2float(v_scale[srow + i]);
-        }
-      } else {
-        const uint16_t* kc = reinterpret_cast<const uint16_t*>(k_cache) + brow + (int64_t)hq * D;
-#pragma unroll
-        for (int j = 0; j < SH::KLOADS; ++j)
-          kw[u][j] = ld_stream<u32x4>(kc + 32 * j + 8 * grp);
-        const uint16_t* vc = reinterpret_cast<const uint16_t*>(v_cache) + brow;
-#pragma unroll
-        for (int i = 0; i < SH::VLOADS; ++i)
-          vw[u][i] = ld_stream<u32x4>(vc + (int64_t)(i * SH::TPW + ts) * D + 8 * c8);
-      }
-    }
-    // ---- scores on MFMA ---------------------------------------------------------------
-    float sc[U][4];
-    float cmax = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (I8) {
-#pragma unroll
-        for (int jj = 0; jj < SH::KLOADS; ++jj)
-#pragma unroll
-          for (int sub = 0; sub < 2; ++sub) {
-            const uint32_t w0 = kw[u][jj][2 * sub] ^ 0x80808080u;
-            const uint32_t w1 = kw[u][jj][2 * sub + 1] ^ 0x80808080u;
-            const u32x4 hv = {widen_lo(w0), widen_hi(w0), widen_lo(w1), widen_hi(w1)};
-            a4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, hv),
-                                                        qf[2 * jj + sub], a4, 0, 0, 0);
-          }
-      } else {
-#pragma unroll
-        for (int j = 0; j < SH::KSTEPS; ++j)
-          a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw[u][j]), qf[j], a4, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t_begin + (blk0 + u) * BS + 4 * grp + i;
-        const bool vis = okb[u] && t >= lo && t < t_end;
-        float s;
-        if constexpr (I8)
-          s = (a4[i] - bias) * ksc[u][i] * scale_log2;
-        else
-          s = a4[i] * scale_log2;
-        sc[u][i] = vis ? s : -INFINITY;
-        cmax = fmaxf(cmax, sc[u][i]);
-      }
-    }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-    cmax = max_x32(cmax);
-    // lazy rescale: move the running max only when it grows by more than 8 (log2 units)
-    if (__builtin_amdgcn_ballot_w64(cmax > m_run + 8.0f) != 0) {
-      const float m_new = fmaxf(m_run, cmax);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_part *= alpha;
-      ps_part *= alpha;
-      if (grp == 0 && hq < GP) s_alpha[wave][hq] = alpha;
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int h = 0; h < GP; ++h) {
-        const float al = s_alpha[wave][h];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] *= al;
-      }
-    }
-    // probabilities -> LDS
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = fast_exp2(sc[u][i] - m_run);
-        l_part += p;
-        if constexpr (I8) {
-          // masked tokens: p = 0 exactly, and their (possibly NaN) scale is not used
-          const _Float16 pv16 = (_Float16)(sc[u][i] == -INFINITY ? 0.f : p * vsc[u][i]);
-          ps_part += (float)pv16;
-          const int t = 4 * grp + i;  // token inside block u: pair t & 7, element t >> 3
-          if (hq < GP)
-            reinterpret_cast<_Float16*>(&s_pp[wave][u][t & 7][hq])[t >> 3] = pv16;
-        } else {
-          if (hq < GP) s_p[wave][u * BS + 4 * grp + i][hq] = p;
-        }
-      }
-    __builtin_amdgcn_wave_barrier();
-    // ---- PV on the VALU -----------------------------------------------------------------
-    if constexpr (I8) {
-      // lane (ts, c8) owns tokens ts + TPW*i of each block; it pairs t = ts + TPW*pr with t + 8
-      // and accumulates p'_t (1152 + x_t[d]) with v_dot2_f32_f16 (codes are finite, masked
-      // tokens have p' = 0)
-      constexpr int NPAIR = SH::VLOADS / 2;
-      static_assert(SH::TPW * NPAIR == 8, "token pairs are (t, t + 8)");
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int pr = 0; pr < NPAIR; ++pr) {
-          const int pair = ts + SH::TPW * pr;
-          const u32x2 bw = vw[u][pr], cw = vw[u][pr + NPAIR];
-          uint32_t xp[8];  // fp16 pairs (1152 + x_t, 1152 + x_{t+8}) for the lane's 8 d
-#pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            const uint32_t bx = bw[k] ^ 0x80808080u, cx = cw[k] ^ 0x80808080u;
-            const uint32_t i0 = __builtin_amdgcn_perm(cx, bx, 0x05010400u);  // b0 c0 b1 c1
-            const uint32_t i1 = __builtin_amdgcn_perm(cx, bx, 0x07030602u);  // b2 c2 b3 c3
-            xp[4 * k + 0] = widen_lo(i0);
-            xp[4 * k + 1] = widen_hi(i0);
-            xp[4 * k + 2] = widen_lo(i1);
-            xp[4 * k + 3] = widen_hi(i1);
-          }
-          uint32_t pp[GP];
-#pragma unroll
-          for (int h4 = 0; h4 < GP; h4 += 4) {
-            if constexpr (GP >= 4) {
-              const u32x4 p4 = *reinterpret_cast<const u32x4*>(&s_pp[wave][u][pair][h4]);
-              pp[h4] = p4[0]; pp[h4 + 1] = p4[1]; pp[h4 + 2] = p4[2]; pp[h4 + 3] = p4[3];
-            } else {
-#pragma unroll
-              for (int h = 0; h < GP; ++h) pp[h] = s_pp[wave][u][pair][h];
-            }
-          }
-#pragma unroll
-          for (int h = 0; h < GP; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              acc[h][e] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pp[h]),
-                                                 __builtin_bit_cast(f16x2, xp[e]), acc[h][e], false);
-        }
-    } else {
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int i = 0; i < SH::VLOADS; ++i) {
-          const int slot = i * SH::TPW + ts;
-          const int tpos = t_begin + (blk0 + u) * BS + slot;
-          if (!(okb[u] && tpos >= lo && tpos < t_end)) continue;  // masked slot may hold NaN
-          float x[8];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[2 * e] = bf16_lo(vw[u][i][e]);
-            x[2 * e + 1] = bf16_hi(vw[u][i][e]);
-          }
-          float pv[GP];
-#pragma unroll
-          for (int h4 = 0; h4 < GP; h4 += 4) {
-            if constexpr (GP >= 4) {
-              const f32x4 p4 = *reinterpret_cast<const f32x4*>(&s_p[wave][u * BS + slot][h4]);
-              pv[h4] = p4[0]; pv[h4 + 1] = p4[1]; pv[h4 + 2] = p4[2]; pv[h4 + 3] = p4[3];
-            } else {
-#pragma unroll
-              for (int h = 0; h < GP; ++h) pv[h] = s_p[wave][u * BS + slot][h];
-            }
-          }
-#pragma unroll
-          for (int h = 0; h < GP; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pv[h], x[e], acc[h][e]);
-        }
-    }
-    __builtin_amdgcn_wave_barrier();  // the staging slices are rewritten by the next chunk
+    c.t0 = t_begin + blk0 * BS;
+    w.load(c, k_cache, v_cache, k_scale, v_scale, Hkv, g);
+  };
+  for (int ch = wave; ch < nchunk; ch += kDecodeWaves) {
+    prep(cA, ch);
+    w.compute(cA, lo, t_end, scale_log2, s_lds[wave]);
   }
 
-  // ---- reduce inside the wave ------------------------------------------------------------
-  // row sums: lanes hq, hq+16, hq+32, hq+48
-  float l_w = l_part + __shfl_xor(l_part, 16);
-  l_w = sum_x32(l_w);
-  float ps_w = 0.f;
-  if constexpr (I8) {
-    ps_w = ps_part + __shfl_xor(ps_part, 16);
-    ps_w = sum_x32(ps_w);
+  float l_w, ps_w;
+  w.reduce(l_w, ps_w);
+  if (w.grp == 0 && w.hq < GP) {
+    s_ml[wave][0][w.hq] = w.m_run;
+    s_ml[wave][1][w.hq] = l_w;
   }
-  // PV accumulators: lanes with equal c8
+  if (w.ts == 0) {
 #pragma unroll
-  for (int h = 0; h < GP; ++h)
+    for (int h = 0; h < GP; ++h)
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-      for (int o = SH::CPR; o < 64; o <<= 1) acc[h][e] += __shfl_xor(acc[h][e], o);
-  if (grp == 0 && hq < GP) {
-    s_ml[wave][0][hq] = m_run;
-    s_ml[wave][1][hq] = l_w;
-    s_ml[wave][2][hq] = ps_w;
-  }
-  __builtin_amdgcn_wave_barrier();
-  if (ts == 0) {
-#pragma unroll
-    for (int h = 0; h < GP; ++h) {
-      const float corr = I8 ? kI8Bias * s_ml[wave][2][h] : 0.f;  // remove the +1152 of the codes
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s_red[wave][h][8 * c8 + e] = acc[h][e] - corr;
-    }
+      for (int e = 0; e < 8; ++e) s_red[wave][h][8 * w.c8 + e] = w.acc[h][e];
   }
   __syncthreads();
 
@@ -410,13 +475,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     const int h = i / D, d = i % D;
     float M = s_ml[0][0][h];
 #pragma unroll
-    for (int w = 1; w < kDecodeWaves; ++w) M = fmaxf(M, s_ml[w][0][h]);
+    for (int wv = 1; wv < kDecodeWaves; ++wv) M = fmaxf(M, s_ml[wv][0][h]);
     float num = 0.f, den = 0.f;
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
-      const float wt = fast_exp2(s_ml[w][0][h] - M);  // waves that saw no token: l = 0, acc = 0
-      num = fmaf(wt, s_red[w][h][d], num);
-      den = fmaf(wt, s_ml[w][1][h], den);
+    for (int wv = 0; wv < kDecodeWaves; ++wv) {
+      const float wt = fast_exp2(s_ml[wv][0][h] - M);  // waves that saw no token: l = 0, acc = 0
+      num = fmaf(wt, s_red[wv][h][d], num);
+      den = fmaf(wt, s_ml[wv][1][h], den);
     }
     const float inv = 1.0f / den;
     const int head = g * G + h;
@@ -430,7 +495,49 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
   }
 }
 
-// Merge the partials of one (sequence, query head): weights exp2(lse_s - max lse).
+// Log-sum-exp merge of n partials (o_i, lse_i in log2 units) of one (sequence, query head),
+// partial i at index first + i * stride, in one pass: the running max moves as partials
+// arrive, and the loads of four partials are in flight together. One wave; lane l owns
+// d = l + 64e. A partial whose piece saw no usable token has lse = -inf and weight 0.
+template <int D>
+__device__ __forceinline__ void merge_partials(const float* __restrict__ part_o,
+                                               const float* __restrict__ part_lse,
+                                               int64_t first, int64_t stride, int n,
+                                               uint16_t* __restrict__ orow) {
+  constexpr int EPT = D / 64, BATCH = 4;
+  const int lane = threadIdx.x;
+  float M = -INFINITY, L = 0.f, acc[EPT] = {};
+  for (int i = 0; i < n; i += BATCH) {
+    float ls[BATCH], ov[BATCH][EPT];
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const int64_t idx = first + (int64_t)(i + k) * stride;
+      ls[k] = i + k < n ? part_lse[idx] : -INFINITY;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) ov[k][e] = i + k < n ? part_o[idx * D + lane + 64 * e] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      if (ls[k] == -INFINITY) continue;
+      if (ls[k] > M) {
+        const float r = fast_exp2(M - ls[k]);  // M = -inf at first: r = 0
+        L *= r;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) acc[e] *= r;
+        M = ls[k];
+      }
+      const float w = fast_exp2(ls[k] - M);
+      L += w;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) acc[e] = fmaf(w, ov[k][e], acc[e]);
+    }
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) orow[lane + 64 * e] = (uint16_t)f32_to_bf16_bits(acc[e] * inv);
+}
+
+// Fixed split: partials of (b, h) are the n_valid splits that hold tokens.
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse,
@@ -441,22 +548,186 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
   const int lo = window > 0 ? max(0, ctx - window) : 0;
   const int base = lo & ~15;
   const int n_valid = ctx > 0 ? min(n_split, (ctx - base + C - 1) / C) : 0;
-  const int64_t pi = ((int64_t)b * Hq + h) * n_split;
-  float M = -INFINITY;
-  for (int s = 0; s < n_valid; ++s) M = fmaxf(M, part_lse[pi + s]);
-  constexpr int EPT = D / 64;
-  float acc[EPT] = {};
-  float L = 0.f;
-  for (int s = 0; s < n_valid; ++s) {
-    const float w = fast_exp2(part_lse[pi + s] - M);
-    L += w;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) acc[e] = fmaf(w, part_o[(pi + s) * D + threadIdx.x + 64 * e], acc[e]);
+  merge_partials<D>(part_o, part_lse, ((int64_t)b * Hq + h) * n_split, 1, n_valid,
+                    out + ((int64_t)b * Hq + h) * D);
+}
+
+// ---- balanced: persistent waves over equal ranges of the (b, g, block) list -----------------
+// Sequence b contributes nvis(b) blocks per KV head (the blocks holding positions
+// [lo_b, ctx_b)); the list orders blocks by (b, g, block). With T = Hkv * sum nvis and P waves,
+// wave p owns list entries [p*q, min((p+1)*q, T)), q = ceil(T / P). The piece of segment
+// s = b*Hkv + g that wave p holds goes to partial slot s + p: pieces of one segment sit in
+// consecutive waves and segments follow in wave order, so the slots are distinct and there
+// are at most B*Hkv + P of them.
+__device__ __forceinline__ int visible_blocks(const int32_t* __restrict__ ctx_lens, int b,
+                                              int max_ctx, int max_blocks, int window) {
+  const int ctx = decode_ctx(ctx_lens, b, max_ctx, max_blocks, 16);
+  if (ctx <= 0) return 0;
+  const int lo = window > 0 ? max(0, ctx - window) : 0;
+  return (ctx + 15) / 16 - lo / 16;
+}
+
+template <int D, int GP, bool I8>
+__global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
+    const uint16_t* __restrict__ q, const void* __restrict__ k_cache,
+    const void* __restrict__ v_cache, const __half* __restrict__ k_scale,
+    const __half* __restrict__ v_scale, const int32_t* __restrict__ table,
+    const int32_t* __restrict__ ctx_lens, uint16_t* __restrict__ out,
+    int32_t* __restrict__ prefix_out, float* __restrict__ part_o, float* __restrict__ part_lse,
+    int B, int Hq, int Hkv, int G, int max_blocks, int num_blocks, int max_ctx,
+    float scale_log2, int window) {
+  using W = DecodeWave<D, GP, I8>;
+  constexpr int BS = W::BS, U = W::U;
+  __shared__ typename W::Lds s_lds[kDecodeWaves];
+  __shared__ int s_pre[kStreamMaxB + 1];
+  __shared__ int s_scan[kDecodeThreads];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // ---- prefix of visible blocks over the sequences (every workgroup; workgroup 0 also
+  // stores it for the merge) --------------------------------------------------------------
+  {
+    const int per = (B + kDecodeThreads - 1) / kDecodeThreads;
+    const int b0 = tid * per;
+    int run = 0;
+    for (int i = 0; i < per && b0 + i < B; ++i)
+      run += visible_blocks(ctx_lens, b0 + i, max_ctx, max_blocks, window);
+    s_scan[tid] = run;
+    __syncthreads();
+    for (int o = 1; o < kDecodeThreads; o <<= 1) {  // inclusive scan
+      const int add = tid >= o ? s_scan[tid - o] : 0;
+      __syncthreads();
+      s_scan[tid] += add;
+      __syncthreads();
+    }
+    run = tid > 0 ? s_scan[tid - 1] : 0;
+    for (int i = 0; i < per && b0 + i < B; ++i) {
+      s_pre[b0 + i] = run;
+      run += visible_blocks(ctx_lens, b0 + i, max_ctx, max_blocks, window);
+    }
+    if (tid == kDecodeThreads - 1) s_pre[B] = s_scan[tid];
+    __syncthreads();
+    if (blockIdx.x == 0)
+      for (int i = tid; i <= B; i += kDecodeThreads) prefix_out[i] = s_pre[i];
   }
-  const float inv = n_valid > 0 ? 1.0f / L : 0.f;
+
+  const int64_t T = (int64_t)Hkv * s_pre[B];
+  const int P = gridDim.x * kDecodeWaves;
+  const int64_t qn = (T + P - 1) / P;
+  const int p = blockIdx.x * kDecodeWaves + wave;
+  int64_t pos = p * qn;
+  const int64_t end = min(pos + qn, T);
+  if (pos >= end) return;  // no barrier follows
+
+  // the segment holding entry pos: the last b with Hkv * pre[b] <= pos (it has nvis(b) > 0)
+  int b = 0;
+  {
+    int lo_b = 0, hi_b = B - 1;
+    while (lo_b < hi_b) {
+      const int mid = (lo_b + hi_b + 1) >> 1;
+      if ((int64_t)Hkv * s_pre[mid] <= pos) lo_b = mid; else hi_b = mid - 1;
+    }
+    b = lo_b;
+  }
+  int nv = s_pre[b + 1] - s_pre[b];
+  int g = (int)((pos - (int64_t)Hkv * s_pre[b]) / nv);
+
+  W w;
+  w.init(lane);
+  while (true) {
+    const int64_t seg0 = (int64_t)Hkv * s_pre[b] + (int64_t)g * nv;
+    const int64_t pend = min(end, seg0 + nv);
+    const int j0 = (int)(pos - seg0), j1 = (int)(pend - seg0);
+    const int ctx = decode_ctx(ctx_lens, b, max_ctx, max_blocks, BS);
+    const int lo = window > 0 ? max(0, ctx - window) : 0;
+    const int lb0 = lo / BS;  // first visible block
+    const int32_t* trow = table + (int64_t)b * max_blocks + lb0;
+
+    const int hi = min((lb0 + j1) * BS, ctx);
+    // the piece's table entries, 64 at a time: lane i holds entry win + i
+    int win = j0;
+    int tab = j0 + lane < j1 ? trow[j0 + lane] : -1;
+    typename W::Chunk cA;
+    auto prep = [&](typename W::Chunk& c, int j) {
 #pragma unroll
-  for (int e = 0; e < EPT; ++e)
-    out[((int64_t)b * Hq + h) * D + threadIdx.x + 64 * e] = (uint16_t)f32_to_bf16_bits(acc[e] * inv);
+      for (int u = 0; u < U; ++u) {
+        int e = -1;
+        if (j + u < j1) {
+          if (j + u - win >= 64) {
+            win += 64;
+            tab = win + lane < j1 ? trow[win + lane] : -1;
+          }
+          e = __builtin_amdgcn_readlane(tab, j + u - win);
+        }
+        c.okb[u] = e >= 0 && e < num_blocks;  // unusable entry: its tokens are skipped
+        c.pb[u] = c.okb[u] ? e : 0;
+      }
+      c.t0 = (lb0 + j) * BS;
+      w.load(c, k_cache, v_cache, k_scale, v_scale, Hkv, g);
+    };
+
+    w.load_q(q + ((int64_t)b * Hq + g * G) * D, G);
+    w.reset();
+    for (int j = j0; j < j1; j += U) {
+      prep(cA, j);
+      w.compute(cA, lo, hi, scale_log2, s_lds[wave]);
+    }
+    float l_w, ps_w;
+    w.reduce(l_w, ps_w);
+    const bool whole = j0 == 0 && j1 == nv;
+    const int64_t slot = (int64_t)b * Hkv + g + p;
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+      const float lh = __shfl(l_w, h), mh = __shfl(w.m_run, h);
+      if (h < G && w.ts == 0) {
+        const float inv = lh > 0.f ? 1.0f / lh : 0.f;
+        if (whole) {
+          u32x4 o4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o4[e] = pack_bf16x2(w.acc[h][2 * e] * inv, w.acc[h][2 * e + 1] * inv);
+          *reinterpret_cast<u32x4*>(out + ((int64_t)b * Hq + g * G + h) * D + 8 * w.c8) = o4;
+        } else {
+          float* po = part_o + ((slot * G + h) * D + 8 * w.c8);
+          f32x4 a = {w.acc[h][0] * inv, w.acc[h][1] * inv, w.acc[h][2] * inv, w.acc[h][3] * inv};
+          f32x4 c = {w.acc[h][4] * inv, w.acc[h][5] * inv, w.acc[h][6] * inv, w.acc[h][7] * inv};
+          *reinterpret_cast<f32x4*>(po) = a;
+          *reinterpret_cast<f32x4*>(po + 4) = c;
+          if (w.c8 == 0) part_lse[slot * G + h] = lh > 0.f ? mh + __log2f(lh) : -INFINITY;
+        }
+      }
+    }
+    pos = pend;
+    if (pos >= end) break;
+    if (++g == Hkv) {  // next sequence with visible blocks (one exists: pos < T)
+      g = 0;
+      do ++b; while (s_pre[b + 1] == s_pre[b]);
+      nv = s_pre[b + 1] - s_pre[b];
+    }
+  }
+}
+
+// Merge for the balanced shape: (b, head h) gathers the pieces of segment (b, h / G) from
+// slots s + p0 .. s + p1; a segment held by one wave was written directly.
+template <int D>
+__global__ __launch_bounds__(64) void decode_stream_merge_kernel(
+    const int32_t* __restrict__ prefix, const float* __restrict__ part_o,
+    const float* __restrict__ part_lse, uint16_t* __restrict__ out, int B, int Hq, int Hkv,
+    int G, int P) {
+  const int h = blockIdx.x, b = blockIdx.y, g = h / G, hl = h % G;
+  const int nv = prefix[b + 1] - prefix[b];
+  uint16_t* orow = out + ((int64_t)b * Hq + h) * D;
+  if (nv == 0) {  // empty context: zeros
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) orow[threadIdx.x + 64 * e] = 0;
+    return;
+  }
+  const int64_t T = (int64_t)Hkv * prefix[B];
+  const int64_t qn = (T + P - 1) / P;
+  const int64_t seg0 = (int64_t)Hkv * prefix[b] + (int64_t)g * nv;
+  const int64_t p0 = seg0 / qn, p1 = (seg0 + nv - 1) / qn;
+  if (p0 == p1) return;
+  const int64_t s = (int64_t)b * Hkv + g;
+  merge_partials<D>(part_o, part_lse, (s + p0) * G + hl, G, (int)(p1 - p0 + 1), orow);
 }
 
 static int pow2_at_least(int g) {
@@ -465,16 +736,44 @@ static int pow2_at_least(int g) {
   return p;
 }
 
+static int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0) {
+    (void)hipGetLastError();
+    return 256;  // MI355X
+  }
+  return cus;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int max_context_len, int window,
                        int split_tokens) {
-  (void)Hq;
   DecodePlan p{};
   const int span = window > 0 ? std::min(max_context_len, window + 15) : max_context_len;
+  if (split_tokens == 0 && window == 0 && B <= kStreamMaxB) {
+    // balanced shape (no window: context lengths, and so the work per sequence, can be
+    // arbitrarily ragged): at most one wave per list entry, and no more waves than the GPU
+    // holds at once (32 per CU for 256-thread workgroups)
+    const int64_t max_entries = (int64_t)B * Hkv * ((span + 15) / 16 + 1);
+    const int64_t waves = std::min<int64_t>((int64_t)device_cus() * 32, max_entries);
+    p.stream = true;
+    p.stream_waves_max = (int)std::max<int64_t>(kDecodeWaves, waves);
+    const size_t slots = (size_t)B * Hkv + p.stream_waves_max;
+    const int G = Hq / Hkv;
+    p.prefix_off = 0;
+    p.part_o_off = align256((size_t)(B + 1) * sizeof(int32_t));
+    p.part_lse_off = p.part_o_off + align256(slots * G * D * sizeof(float));
+    p.workspace_bytes = p.part_lse_off + slots * G * sizeof(float);
+    return p;
+  }
   int C = split_tokens;
   if (C == 0) {
-    // 2048-token splits for long spans, 1024 otherwise (a quarter of the span, at least 256,
-    // for short contexts): enough workgroups to balance ragged contexts over the CUs, few
-    // enough that the per-split prologue and the merge stay small (measured on MI355X).
+    // fixed splits chosen by the library (a window bounds every sequence's span, or the batch
+    // is too large for the balanced shape): 2048-token splits for long spans, else a quarter of
+    // the span rounded to 256 within [256, 1024] (measured on MI355X)
     if (span >= 8192)
       C = 2048;
     else
@@ -486,58 +785,78 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int max_context_len, int w
     p.workspace_bytes = 0;
   } else {
     const size_t parts = (size_t)B * Hq * p.n_split;
-    const size_t o_bytes = parts * D * sizeof(float);
-    const size_t lse_off = (o_bytes + 255) & ~(size_t)255;
-    p.workspace_bytes = lse_off + parts * sizeof(float);
+    p.part_o_off = 0;
+    p.part_lse_off = align256(parts * D * sizeof(float));
+    p.workspace_bytes = p.part_lse_off + parts * sizeof(float);
   }
   return p;
 }
 
-int launch_decode(const DecodeArgs& a, hipStream_t stream) {
+template <int D, int GP, bool I8>
+static void launch_stream(const DecodeArgs& a, hipStream_t stream) {
+  const auto kern = decode_stream_kernel<D, GP, I8>;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kDecodeThreads, 0) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  const int wgs = std::max(1, std::min(device_cus() * per_cu, a.plan.stream_waves_max / kDecodeWaves));
+  char* ws = reinterpret_cast<char*>(a.workspace);
+  int32_t* prefix = reinterpret_cast<int32_t*>(ws + a.plan.prefix_off);
+  float* part_o = reinterpret_cast<float*>(ws + a.plan.part_o_off);
+  float* part_lse = reinterpret_cast<float*>(ws + a.plan.part_lse_off);
   const int G = a.Hq / a.Hkv;
-  const int GP = pow2_at_least(G);
+  hipLaunchKernelGGL(kern, dim3(wgs), dim3(kDecodeThreads), 0, stream, (const uint16_t*)a.q,
+                     a.k_cache, a.v_cache, (const __half*)a.k_scale, (const __half*)a.v_scale,
+                     a.block_table, a.context_lens, (uint16_t*)a.o, prefix, part_o, part_lse, a.B,
+                     a.Hq, a.Hkv, G, a.max_blocks_per_seq, a.num_blocks, a.max_context_len,
+                     a.scale * kLog2e, a.window);
+  hipLaunchKernelGGL(decode_stream_merge_kernel<D>, dim3(a.Hq, a.B), dim3(64), 0, stream, prefix,
+                     part_o, part_lse, (uint16_t*)a.o, a.B, a.Hq, a.Hkv, G, wgs * kDecodeWaves);
+}
+
+template <int D, int GP, bool I8>
+static void launch_split(const DecodeArgs& a, hipStream_t stream) {
+  const int G = a.Hq / a.Hkv;
   const int C = a.plan.split_tokens, ns = a.plan.n_split;
-  float* part_o = nullptr;
-  float* part_lse = nullptr;
-  if (ns > 1) {
-    const size_t parts = (size_t)a.B * a.Hq * ns;
-    const size_t lse_off = (parts * a.D * sizeof(float) + 255) & ~(size_t)255;
-    part_o = reinterpret_cast<float*>(a.workspace);
-    part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(a.workspace) + lse_off);
+  char* ws = reinterpret_cast<char*>(a.workspace);
+  float* part_o = ns > 1 ? reinterpret_cast<float*>(ws + a.plan.part_o_off) : nullptr;
+  float* part_lse = ns > 1 ? reinterpret_cast<float*>(ws + a.plan.part_lse_off) : nullptr;
+  hipLaunchKernelGGL((decode_split_kernel<D, GP, I8>), dim3(a.Hkv, a.B, ns), dim3(kDecodeThreads),
+                     0, stream, (const uint16_t*)a.q, a.k_cache, a.v_cache,
+                     (const __half*)a.k_scale, (const __half*)a.v_scale, a.block_table,
+                     a.context_lens, (uint16_t*)a.o, part_o, part_lse, a.Hq, a.Hkv, G,
+                     a.max_blocks_per_seq, a.num_blocks, a.max_context_len, a.scale * kLog2e,
+                     a.window, C, ns);
+  if (ns > 1)
+    hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(a.Hq, a.B), dim3(64), 0, stream, part_o,
+                       part_lse, a.context_lens, (uint16_t*)a.o, a.Hq, a.max_blocks_per_seq,
+                       a.max_context_len, a.window, C, ns);
+}
+
+template <int D, int GP, bool I8>
+static void launch_shape(const DecodeArgs& a, hipStream_t stream) {
+  if (a.plan.stream)
+    launch_stream<D, GP, I8>(a, stream);
+  else
+    launch_split<D, GP, I8>(a, stream);
+}
+
+template <int D, bool I8>
+static void launch_g(const DecodeArgs& a, hipStream_t stream) {
+  switch (pow2_at_least(a.Hq / a.Hkv)) {
+    case 1: launch_shape<D, 1, I8>(a, stream); break;
+    case 2: launch_shape<D, 2, I8>(a, stream); break;
+    case 4: launch_shape<D, 4, I8>(a, stream); break;
+    case 8: launch_shape<D, 8, I8>(a, stream); break;
+    default: launch_shape<D, 16, I8>(a, stream); break;
   }
-  const float scale_log2 = a.scale * kLog2e;
-  dim3 grid(a.Hkv, a.B, ns);
-#define ATTN_DSPLIT(DD, GG, I8)                                                                 \
-  hipLaunchKernelGGL((decode_split_kernel<DD, GG, I8>), grid, dim3(kDecodeThreads), 0, stream, \
-                     (const uint16_t*)a.q, a.k_cache, a.v_cache, (const __half*)a.k_scale,      \
-                     (const __half*)a.v_scale, a.block_table, a.context_lens, (uint16_t*)a.o,   \
-                     part_o, part_lse, a.Hq, a.Hkv, G, a.max_blocks_per_seq, a.num_blocks,      \
-                     a.max_context_len, scale_log2, a.window, C, ns)
-#define ATTN_DSPLIT_G(DD, I8)                 \
-  switch (GP) {                               \
-    case 1: ATTN_DSPLIT(DD, 1, I8); break;    \
-    case 2: ATTN_DSPLIT(DD, 2, I8); break;    \
-    case 4: ATTN_DSPLIT(DD, 4, I8); break;    \
-    case 8: ATTN_DSPLIT(DD, 8, I8); break;    \
-    default: ATTN_DSPLIT(DD, 16, I8); break;  \
-  }
+}
+
+int launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.D == 64) {
-    if (a.int8) { ATTN_DSPLIT_G(64, true) } else { ATTN_DSPLIT_G(64, false) }
+    if (a.int8) launch_g<64, true>(a, stream); else launch_g<64, false>(a, stream);
   } else {
-    if (a.int8) { ATTN_DSPLIT_G(128, true) } else { ATTN_DSPLIT_G(128, false) }
-  }
-#undef ATTN_DSPLIT_G
-#undef ATTN_DSPLIT
-  if (ns > 1) {
-    dim3 mgrid(a.Hq, a.B);
-    if (a.D == 64)
-      hipLaunchKernelGGL(decode_merge_kernel<64>, mgrid, dim3(64), 0, stream, part_o, part_lse,
-                         a.context_lens, (uint16_t*)a.o, a.Hq, a.max_blocks_per_seq,
-                         a.max_context_len, a.window, C, ns);
-    else
-      hipLaunchKernelGGL(decode_merge_kernel<128>, mgrid, dim3(64), 0, stream, part_o, part_lse,
-                         a.context_lens, (uint16_t*)a.o, a.Hq, a.max_blocks_per_seq,
-                         a.max_context_len, a.window, C, ns);
+    if (a.int8) launch_g<128, true>(a, stream); else launch_g<128, false>(a, stream);
   }
   return 0;
 }

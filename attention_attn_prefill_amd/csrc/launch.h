@@ -19,10 +19,14 @@ struct PrefillArgs {
 };
 
 constexpr int kMaxSplitTokens = 8192;  // largest split_tokens a decode call accepts
+constexpr int kStreamMaxB = 2048;      // largest batch of the balanced decode shape
 
 struct DecodePlan {
-  int split_tokens;  // tokens per workgroup along the KV axis (multiple of 16)
-  int n_split;       // workgroups per (sequence, KV head)
+  bool stream;           // balanced persistent shape (else fixed splits)
+  int stream_waves_max;  // balanced: most waves a launch may use (sizes the partial slots)
+  int split_tokens;      // fixed split: tokens per workgroup along the KV axis (multiple of 16)
+  int n_split;           // fixed split: workgroups per (sequence, KV head)
+  size_t prefix_off, part_o_off, part_lse_off;  // workspace layout (bytes)
   size_t workspace_bytes;
 };
 

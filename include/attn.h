@@ -133,9 +133,13 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_context
  *  max_context_len : host-side upper bound of context_lens, used to plan the split of the
  *                 KV range across workgroups without reading device memory.
  *  window       : 0 = no window; else only the last `window` positions are attended.
- *  split_tokens : tokens per workgroup along the KV axis: 0 = the library's choice, else a
- *                 positive multiple of block_size, at most 8192 (ATTN_ERR_UNSUPPORTED above).
- *                 Partials are merged by log-sum-exp.
+ *  split_tokens : how the KV axis is divided, partials merged by log-sum-exp. 0 = the
+ *                 library's choice: with window == 0 and B <= 2048, a persistent grid whose
+ *                 waves take equal shares of all (sequence, KV head, block) work, so ragged
+ *                 contexts stay balanced; otherwise fixed splits sized from max_context_len.
+ *                 Else a positive multiple of block_size, at most 8192
+ *                 (ATTN_ERR_UNSUPPORTED above): fixed splits of that many tokens.
+ *                 Results are run-to-run identical for a given split_tokens on a given GPU.
  *  workspace    : device buffer of at least attn_decode_workspace_size(...) bytes (may be NULL
  *                 when that size is 0); overwritten by the call; its contents on entry do not
  *                 matter. Two calls in flight at once must not share a workspace.

@@ -97,6 +97,10 @@ def test_workspace_size_rules():
     assert n >= 2 * 8 * 79 * (64 + 1) * 4
     assert ws(2, 8, 2, 64, 5000, 100, 64) < n  # the window bounds the splits
     assert ws(0, 8, 2, 64, 64, 0, 0) == 0
+    # library's choice, no window: the balanced shape always stages partials (prefix + slots)
+    assert ws(2, 8, 2, 64, 64, 0, 0) >= (2 * 2 + 4) * 4 * (64 + 1) * 4
+    # library's choice with a window covering the whole span: one split, no workspace
+    assert ws(2, 8, 2, 64, 64, 100, 0) == 0
 
 
 def _append(**kw):

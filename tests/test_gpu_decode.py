@@ -115,6 +115,39 @@ def test_split_invariance_and_determinism():
         first = o if first is None else first
 
 
+@pytest.mark.parametrize("kv", ["bf16", "i8"])
+def test_decode_balanced_tiny_and_empty_contexts(kv):
+    """Default (balanced) shape with no window: many short and empty sequences, so one wave's
+    range spans several (sequence, KV head) segments and segments split across waves."""
+    ctx = (0, 1, 2, 15, 16, 17, 0, 33, 1, 100, 48, 0, 5, 64, 65, 3)
+    wl, ctx, table, nb, qbits, qf = _small(64, 8, 2, 0, kv=kv, ctx=ctx, seed=11)
+    live = ctx > 0
+    if kv == "bf16":
+        kb, vb = pool(wl, "k", nb), pool(wl, "v", nb)
+        o = _decode(dev_bf16(qbits), dev_bf16(kb), dev_bf16(vb), dev(table), dev(ctx), wl, 100)
+        ro, _ = oracle.decode_paged(qf[live], bf16_value(kb), bf16_value(vb), table[live], ctx[live],
+                                    wl.scale, 16)
+    else:
+        (kc, ks), (vc, vs) = int8_pool(wl, "k", nb), int8_pool(wl, "v", nb)
+        o = _decode(dev_bf16(qbits), dev(kc), dev(vc), dev(table), dev(ctx), wl, 100, ks=dev(ks), vs=dev(vs))
+        ro, _ = oracle.decode_paged(qf[live], kc, vc, table[live], ctx[live], wl.scale, 16,
+                                    k_scale=ks, v_scale=vs)
+    got = host_f64(o)
+    assert (got[~live] == 0).all()
+    assert maxabs(got[live], ro) <= BF16_TOL
+
+
+def test_decode_large_batch_uses_fixed_splits():
+    """Beyond the balanced shape's batch limit the default falls back to fixed splits."""
+    rng = np.random.default_rng(5)
+    ctx = tuple(int(c) for c in rng.integers(1, 40, size=2100))
+    wl, ctx, table, nb, qbits, qf = _small(64, 8, 2, 0, ctx=ctx, spare=0, seed=12)
+    kb, vb = pool(wl, "k", nb), pool(wl, "v", nb)
+    o = _decode(dev_bf16(qbits), dev_bf16(kb), dev_bf16(vb), dev(table), dev(ctx), wl, 40)
+    ro, _ = oracle.decode_paged(qf, bf16_value(kb), bf16_value(vb), table, ctx, wl.scale, 16)
+    assert maxabs(host_f64(o), ro) <= BF16_TOL
+
+
 def test_zero_context_gives_zero():
     wl, ctx, table, nb, qbits, qf = _small(64, 8, 2, 0, ctx=(5, 3))
     kb, vb = pool(wl, "k", nb), pool(wl, "v", nb)
