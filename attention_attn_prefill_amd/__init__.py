@@ -2,7 +2,8 @@
 
 Every computation runs in the HIP kernels of libattn.so; torch supplies device memory and the
 current stream. The names follow the C ABI in include/attn.h: attn_prefill,
-attn_prefill_paged, attn_decode_paged, kv_cache_append, attn_decode_workspace_size.
+attn_prefill_paged, attn_decode_paged, attn_decode_paged_multi, kv_cache_append,
+attn_decode_workspace_size, attn_decode_multi_workspace_size.
 """
 from __future__ import annotations
 
@@ -27,6 +28,9 @@ _SIGS = {
                                 _I, _I, ctypes.c_float, _I, _I, _P]),
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
                                ctypes.c_float, _I, _I, _P, ctypes.c_size_t, _P]),
+    "attn_decode_multi_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I, _I, _I]),
+    "attn_decode_paged_multi": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
+                                     _I, _I, ctypes.c_float, _I, _I, _P, ctypes.c_size_t, _P]),
     "kv_cache_append": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
     "attn_status_str": (ctypes.c_char_p, [_I]),
     "attn_last_error": (ctypes.c_char_p, []),
@@ -151,6 +155,35 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, max_contex
     _check(lib().attn_decode_paged(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
         _ptr(context_lens), _ptr(out), _dtype_code(k_cache), B, Hq, Hkv, D, bs,
+        block_table.shape[1], num_blocks, int(max_context_len),
+        float(D ** -0.5 if scale is None else scale), int(window), int(split_tokens),
+        _ptr(workspace), ws_bytes, _stream(q)))
+    return out
+
+
+def attn_decode_multi_workspace_size(B, q_len, Hq, Hkv, D, max_context_len, window=0,
+                                     split_tokens=0) -> int:
+    return int(lib().attn_decode_multi_workspace_size(B, q_len, Hq, Hkv, D, max_context_len, window,
+                                                      split_tokens))
+
+
+def attn_decode_paged_multi(q, k_cache, v_cache, block_table, context_lens, max_context_len: int, *,
+                            k_scale=None, v_scale=None, scale: float | None = None, window: int = 0,
+                            split_tokens: int = 0, out=None, workspace=None):
+    """q_len query rows per sequence (speculative verification): q [B][q_len][Hq][D] bf16, row r at
+    position context_lens[b] - q_len + r, causal; caches and table as in attn_decode_paged."""
+    import torch
+    B, QL, Hq, D = q.shape
+    num_blocks, Hkv, bs, _ = k_cache.shape
+    if out is None:
+        out = torch.empty_like(q)
+    need = attn_decode_multi_workspace_size(B, QL, Hq, Hkv, D, max_context_len, window, split_tokens)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().attn_decode_paged_multi(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+        _ptr(context_lens), _ptr(out), _dtype_code(k_cache), B, QL, Hq, Hkv, D, bs,
         block_table.shape[1], num_blocks, int(max_context_len),
         float(D ** -0.5 if scale is None else scale), int(window), int(split_tokens),
         _ptr(workspace), ws_bytes, _stream(q)))

@@ -105,20 +105,31 @@ int attn_prefill_paged(const void* q, const void* k_new, const void* v_new, void
   return check_launch("attn_prefill_paged");
 }
 
-size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_context_len, int window,
-                                  int split_tokens) {
-  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || max_context_len < 1 || window < 0 ||
+static size_t decode_workspace(int B, int q_len, int Hq, int Hkv, int D, int max_context_len,
+                               int window, int split_tokens) {
+  if (B < 1 || q_len < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || max_context_len < 1 || window < 0 ||
       split_tokens < 0)
     return 0;
-  return attn::plan_decode(B, Hq, Hkv, D, max_context_len, window, split_tokens).workspace_bytes;
+  return attn::plan_decode(B, q_len, Hq, Hkv, D, max_context_len, window, split_tokens)
+      .workspace_bytes;
 }
 
-int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
-                      const void* k_scale, const void* v_scale, const int32_t* block_table,
-                      const int32_t* context_lens, void* o, int kv_dtype, int B, int Hq, int Hkv,
-                      int D, int block_size, int max_blocks_per_seq, int num_blocks,
-                      int max_context_len, float scale, int window, int split_tokens,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_context_len, int window,
+                                  int split_tokens) {
+  return decode_workspace(B, 1, Hq, Hkv, D, max_context_len, window, split_tokens);
+}
+
+size_t attn_decode_multi_workspace_size(int B, int q_len, int Hq, int Hkv, int D,
+                                        int max_context_len, int window, int split_tokens) {
+  return decode_workspace(B, q_len, Hq, Hkv, D, max_context_len, window, split_tokens);
+}
+
+static int decode_impl(const char* who, const void* q, const void* k_cache, const void* v_cache,
+                       const void* k_scale, const void* v_scale, const int32_t* block_table,
+                       const int32_t* context_lens, void* o, int kv_dtype, int B, int q_len,
+                       int Hq, int Hkv, int D, int block_size, int max_blocks_per_seq,
+                       int num_blocks, int max_context_len, float scale, int window,
+                       int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k_cache || !v_cache || !block_table || !context_lens || !o)
     return fail(ATTN_ERR_NULL, "q, k_cache, v_cache, block_table, context_lens and o are required");
   if (kv_dtype != ATTN_BF16 && kv_dtype != ATTN_I8)
@@ -127,28 +138,56 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
     return fail(ATTN_ERR_NULL, "int8 cache needs k_scale and v_scale");
   if (kv_dtype == ATTN_BF16 && (k_scale || v_scale))
     return fail(ATTN_ERR_SHAPE, "k_scale/v_scale must be NULL for a bf16 cache");
-  if (B < 1 || Hq < 1 || Hkv < 1 || max_blocks_per_seq < 1 || num_blocks < 1 || max_context_len < 1)
-    return fail(ATTN_ERR_SHAPE, "B, Hq, Hkv, max_blocks_per_seq, num_blocks, max_context_len must be >= 1");
+  if (B < 1 || q_len < 1 || Hq < 1 || Hkv < 1 || max_blocks_per_seq < 1 || num_blocks < 1 ||
+      max_context_len < 1)
+    return fail(ATTN_ERR_SHAPE, "B, q_len, Hq, Hkv, max_blocks_per_seq, num_blocks, max_context_len must be >= 1");
   if (Hq % Hkv != 0) return fail(ATTN_ERR_SHAPE, "Hq %d is not a multiple of Hkv %d", Hq, Hkv);
   if (window < 0) return fail(ATTN_ERR_SHAPE, "window %d < 0", window);
   if (split_tokens < 0) return fail(ATTN_ERR_SHAPE, "split_tokens %d < 0", split_tokens);
   if (!(std::isfinite(scale) && scale > 0.f)) return fail(ATTN_ERR_SHAPE, "scale must be finite and > 0");
   if (!supported_d(D)) return fail(ATTN_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
   if (block_size != 16) return fail(ATTN_ERR_UNSUPPORTED, "block_size %d (supported: 16)", block_size);
-  if (Hq / Hkv > 16) return fail(ATTN_ERR_UNSUPPORTED, "Hq/Hkv = %d > 16", Hq / Hkv);
+  if (Hq / Hkv * q_len > 16)
+    return fail(ATTN_ERR_UNSUPPORTED, "(Hq/Hkv) * q_len = %d > 16", Hq / Hkv * q_len);
   if (split_tokens % block_size != 0) return fail(ATTN_ERR_SHAPE, "split_tokens %d is not a multiple of block_size", split_tokens);
   if (split_tokens > attn::kMaxSplitTokens)
     return fail(ATTN_ERR_UNSUPPORTED, "split_tokens %d > %d", split_tokens, attn::kMaxSplitTokens);
-  if (B > 65535 || Hkv > 65535) return fail(ATTN_ERR_SHAPE, "B and Hkv must be <= 65535");
-  attn::DecodePlan plan = attn::plan_decode(B, Hq, Hkv, D, max_context_len, window, split_tokens);
+  if (B > 65535 / q_len || Hkv > 65535) return fail(ATTN_ERR_SHAPE, "B * q_len and Hkv must be <= 65535");
+  attn::DecodePlan plan =
+      attn::plan_decode(B, q_len, Hq, Hkv, D, max_context_len, window, split_tokens);
   if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
     return fail(ATTN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", plan.workspace_bytes,
                 workspace ? workspace_bytes : (size_t)0);
   attn::DecodeArgs a{q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, o,
-                     kv_dtype == ATTN_I8, B, Hq, Hkv, D, block_size, max_blocks_per_seq,
+                     kv_dtype == ATTN_I8, B, q_len, Hq, Hkv, D, block_size, max_blocks_per_seq,
                      num_blocks, max_context_len, scale, window, plan, workspace};
   attn::launch_decode(a, reinterpret_cast<hipStream_t>(stream));
-  return check_launch("attn_decode_paged");
+  return check_launch(who);
+}
+
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                      const void* k_scale, const void* v_scale, const int32_t* block_table,
+                      const int32_t* context_lens, void* o, int kv_dtype, int B, int Hq, int Hkv,
+                      int D, int block_size, int max_blocks_per_seq, int num_blocks,
+                      int max_context_len, float scale, int window, int split_tokens,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl("attn_decode_paged", q, k_cache, v_cache, k_scale, v_scale, block_table,
+                     context_lens, o, kv_dtype, B, 1, Hq, Hkv, D, block_size, max_blocks_per_seq,
+                     num_blocks, max_context_len, scale, window, split_tokens, workspace,
+                     workspace_bytes, stream);
+}
+
+int attn_decode_paged_multi(const void* q, const void* k_cache, const void* v_cache,
+                            const void* k_scale, const void* v_scale,
+                            const int32_t* block_table, const int32_t* context_lens, void* o,
+                            int kv_dtype, int B, int q_len, int Hq, int Hkv, int D,
+                            int block_size, int max_blocks_per_seq, int num_blocks,
+                            int max_context_len, float scale, int window, int split_tokens,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl("attn_decode_paged_multi", q, k_cache, v_cache, k_scale, v_scale,
+                     block_table, context_lens, o, kv_dtype, B, q_len, Hq, Hkv, D, block_size,
+                     max_blocks_per_seq, num_blocks, max_context_len, scale, window, split_tokens,
+                     workspace, workspace_bytes, stream);
 }
 
 int kv_cache_append(const void* k_new, const void* v_new, const int32_t* seq_idx,

@@ -33,6 +33,7 @@
 #include "launch.h"
 #include <hip/hip_fp16.h>
 #include <algorithm>
+#include <climits>
 #include <type_traits>
 
 namespace attn {
@@ -40,6 +41,11 @@ namespace attn {
 constexpr int kDecodeThreads = 256;
 constexpr int kDecodeWaves = 4;
 constexpr int kMaxSplitBlocks = kMaxSplitTokens / 16;  // the table slice is kept in LDS
+
+// First key any of the QL query rows (positions ctx - QL .. ctx - 1) attends to.
+__device__ __forceinline__ int first_key(int ctx, int QL, int window) {
+  return window > 0 ? max(0, ctx - QL + 1 - window) : 0;
+}
 
 __device__ __forceinline__ int decode_ctx(const int32_t* ctx_lens, int b, int max_ctx,
                                           int max_blocks, int bs) {
@@ -111,6 +117,7 @@ struct DecodeWave {
   float l_part;   // this lane's share of the row sum
   float ps_part;  // INT8: this lane's share of sum(p'), in the fp16 values used
   float acc[GP][8];
+  int qpos, wlo;  // this lane's column: its query position and first key its window admits
 
   __device__ __forceinline__ void init(int lane_) {
     lane = lane_;
@@ -120,17 +127,23 @@ struct DecodeWave {
     ts = lane / SH::CPR;
   }
 
-  // Q^T of heads g*G .. g*G+G-1 (qrow: head g*G of the sequence), padded to 16 columns
-  __device__ __forceinline__ void load_q(const uint16_t* __restrict__ qrow, int G) {
+  // Q^T of the wave's columns, padded to 16: column c < G*QL is query row r = c / G (position
+  // ctx - QL + r) of head g*G + c % G of sequence b; q is [B][QL][Hq][D].
+  __device__ __forceinline__ void load_q(const uint16_t* __restrict__ q, int b, int g, int G,
+                                         int QL, int Hq, int ctx, int window) {
     float qsum = 0.f;
-    qrow += (int64_t)hq * D;
+    const int ncol = G * QL;
+    const int r = hq / G, h = hq % G;
+    const uint16_t* qrow = q + (((int64_t)b * QL + r) * Hq + g * G + h) * D;
+    qpos = ctx - QL + r;
+    wlo = window > 0 ? qpos - window + 1 : INT_MIN;
 #pragma unroll
     for (int j = 0; j < SH::KSTEPS; ++j) {
       // bf16: step j covers d = 32j + 8*grp + e; INT8: one 16-byte load feeds steps 2jj,
       // 2jj+1 covering d = 64*jj + 16*grp + 8*sub + e.
       const int d0 = I8 ? (64 * (j / 2) + 16 * grp + 8 * (j % 2)) : (32 * j + 8 * grp);
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (hq < G) w = *reinterpret_cast<const u32x4*>(qrow + d0);
+      if (hq < ncol) w = *reinterpret_cast<const u32x4*>(qrow + d0);
       if constexpr (I8) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -206,7 +219,8 @@ struct DecodeWave {
     }
   }
 
-  // Online softmax + PV of a loaded chunk; tokens outside [lo, hi) are masked.
+  // Online softmax + PV of a loaded chunk; tokens outside [lo, hi) are masked, and for each
+  // column the tokens after its query position or left of its window.
   __device__ __forceinline__ void compute(const Chunk& c, int lo, int hi, float scale_log2,
                                           Lds& L) {
     // ---- scores on MFMA -----------------------------------------------------------------
@@ -234,7 +248,7 @@ struct DecodeWave {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = c.t0 + u * BS + 4 * grp + i;
-        const bool vis = c.okb[u] && t >= lo && t < hi;
+        const bool vis = c.okb[u] && t >= lo && t < hi && t <= qpos && t >= wlo;
         float s;
         if constexpr (I8)
           s = (a4[i] - bias) * c.ksc[u][i] * scale_log2;
@@ -391,7 +405,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     const void* __restrict__ v_cache, const __half* __restrict__ k_scale,
     const __half* __restrict__ v_scale, const int32_t* __restrict__ table,
     const int32_t* __restrict__ ctx_lens, uint16_t* __restrict__ out,
-    float* __restrict__ part_o, float* __restrict__ part_lse, int Hq, int Hkv, int G,
+    float* __restrict__ part_o, float* __restrict__ part_lse, int Hq, int Hkv, int G, int QL,
     int max_blocks, int num_blocks, int max_ctx, float scale_log2, int window, int C,
     int n_split) {
   using W = DecodeWave<D, GP, I8>;
@@ -408,14 +422,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
+  const int ncol = G * QL;
   const int ctx = decode_ctx(ctx_lens, b, max_ctx, max_blocks, BS);
-  const int lo = window > 0 ? max(0, ctx - window) : 0;
+  const int lo = first_key(ctx, QL, window);
   const int base = lo & ~(BS - 1);
   const int t_begin = base + split * C;
   if (ctx <= 0) {
     if (split == 0 && n_split == 1) {
-      for (int i = threadIdx.x; i < G * D; i += kDecodeThreads)
-        out[((int64_t)b * Hq + g * G) * D + i] = 0;
+      for (int i = threadIdx.x; i < ncol * D; i += kDecodeThreads) {
+        const int c = i / D;
+        out[(((int64_t)b * QL + c / G) * Hq + g * G + c % G) * D + i % D] = 0;
+      }
     }
     return;
   }
@@ -434,7 +451,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
 
   W w;
   w.init(lane);
-  w.load_q(q + ((int64_t)b * Hq + g * G) * D, G);
+  w.load_q(q, b, g, G, QL, Hq, ctx, window);
   w.reset();
   // this wave's chunks are ch = wave, wave + 4, ...
   const int nchunk = (nblk + U - 1) / U;
@@ -471,8 +488,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
   __syncthreads();
 
   // ---- merge the 4 waves and write ---------------------------------------------------------
-  for (int i = threadIdx.x; i < G * D; i += kDecodeThreads) {
-    const int h = i / D, d = i % D;
+  for (int i = threadIdx.x; i < ncol * D; i += kDecodeThreads) {
+    const int h = i / D, d = i % D;  // column h: query row h / G, head g*G + h % G
     float M = s_ml[0][0][h];
 #pragma unroll
     for (int wv = 1; wv < kDecodeWaves; ++wv) M = fmaxf(M, s_ml[wv][0][h]);
@@ -483,12 +500,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
       num = fmaf(wt, s_red[wv][h][d], num);
       den = fmaf(wt, s_ml[wv][1][h], den);
     }
-    const float inv = 1.0f / den;
-    const int head = g * G + h;
+    const float inv = den > 0.f ? 1.0f / den : 0.f;
+    const int64_t orow = ((int64_t)b * QL + h / G) * Hq + g * G + h % G;  // query row, head
     if (n_split == 1) {
-      out[((int64_t)b * Hq + head) * D + d] = (uint16_t)f32_to_bf16_bits(num * inv);
+      out[orow * D + d] = (uint16_t)f32_to_bf16_bits(num * inv);
     } else {
-      const int64_t pi = ((int64_t)b * Hq + head) * n_split + split;
+      const int64_t pi = orow * n_split + split;
       part_o[pi * D + d] = num * inv;
       if (d == 0) part_lse[pi] = M + __log2f(den);
     }
@@ -537,19 +554,18 @@ __device__ __forceinline__ void merge_partials(const float* __restrict__ part_o,
   for (int e = 0; e < EPT; ++e) orow[lane + 64 * e] = (uint16_t)f32_to_bf16_bits(acc[e] * inv);
 }
 
-// Fixed split: partials of (b, h) are the n_valid splits that hold tokens.
+// Fixed split: partials of (query row, head) are the n_valid splits that hold tokens.
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse,
-    const int32_t* __restrict__ ctx_lens, uint16_t* __restrict__ out, int Hq, int max_blocks,
-    int max_ctx, int window, int C, int n_split) {
-  const int h = blockIdx.x, b = blockIdx.y;
+    const int32_t* __restrict__ ctx_lens, uint16_t* __restrict__ out, int Hq, int QL,
+    int max_blocks, int max_ctx, int window, int C, int n_split) {
+  const int h = blockIdx.x, row = blockIdx.y, b = row / QL;  // row: query row b*QL + r
   const int ctx = decode_ctx(ctx_lens, b, max_ctx, max_blocks, 16);
-  const int lo = window > 0 ? max(0, ctx - window) : 0;
-  const int base = lo & ~15;
+  const int base = first_key(ctx, QL, window) & ~15;
   const int n_valid = ctx > 0 ? min(n_split, (ctx - base + C - 1) / C) : 0;
-  merge_partials<D>(part_o, part_lse, ((int64_t)b * Hq + h) * n_split, 1, n_valid,
-                    out + ((int64_t)b * Hq + h) * D);
+  merge_partials<D>(part_o, part_lse, ((int64_t)row * Hq + h) * n_split, 1, n_valid,
+                    out + ((int64_t)row * Hq + h) * D);
 }
 
 // ---- balanced: persistent waves over equal ranges of the (b, g, block) list -----------------
@@ -560,11 +576,10 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
 // consecutive waves and segments follow in wave order, so the slots are distinct and there
 // are at most B*Hkv + P of them.
 __device__ __forceinline__ int visible_blocks(const int32_t* __restrict__ ctx_lens, int b,
-                                              int max_ctx, int max_blocks, int window) {
+                                              int max_ctx, int max_blocks, int window, int QL) {
   const int ctx = decode_ctx(ctx_lens, b, max_ctx, max_blocks, 16);
   if (ctx <= 0) return 0;
-  const int lo = window > 0 ? max(0, ctx - window) : 0;
-  return (ctx + 15) / 16 - lo / 16;
+  return (ctx + 15) / 16 - first_key(ctx, QL, window) / 16;
 }
 
 template <int D, int GP, bool I8>
@@ -574,7 +589,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
     const __half* __restrict__ v_scale, const int32_t* __restrict__ table,
     const int32_t* __restrict__ ctx_lens, uint16_t* __restrict__ out,
     int32_t* __restrict__ prefix_out, float* __restrict__ part_o, float* __restrict__ part_lse,
-    int B, int Hq, int Hkv, int G, int max_blocks, int num_blocks, int max_ctx,
+    int B, int Hq, int Hkv, int G, int QL, int max_blocks, int num_blocks, int max_ctx,
     float scale_log2, int window) {
   using W = DecodeWave<D, GP, I8>;
   constexpr int BS = W::BS, U = W::U;
@@ -591,7 +606,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
     const int b0 = tid * per;
     int run = 0;
     for (int i = 0; i < per && b0 + i < B; ++i)
-      run += visible_blocks(ctx_lens, b0 + i, max_ctx, max_blocks, window);
+      run += visible_blocks(ctx_lens, b0 + i, max_ctx, max_blocks, window, QL);
     s_scan[tid] = run;
     __syncthreads();
     for (int o = 1; o < kDecodeThreads; o <<= 1) {  // inclusive scan
@@ -603,7 +618,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
     run = tid > 0 ? s_scan[tid - 1] : 0;
     for (int i = 0; i < per && b0 + i < B; ++i) {
       s_pre[b0 + i] = run;
-      run += visible_blocks(ctx_lens, b0 + i, max_ctx, max_blocks, window);
+      run += visible_blocks(ctx_lens, b0 + i, max_ctx, max_blocks, window, QL);
     }
     if (tid == kDecodeThreads - 1) s_pre[B] = s_scan[tid];
     __syncthreads();
@@ -639,7 +654,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
     const int64_t pend = min(end, seg0 + nv);
     const int j0 = (int)(pos - seg0), j1 = (int)(pend - seg0);
     const int ctx = decode_ctx(ctx_lens, b, max_ctx, max_blocks, BS);
-    const int lo = window > 0 ? max(0, ctx - window) : 0;
+    const int lo = first_key(ctx, QL, window);
     const int lb0 = lo / BS;  // first visible block
     const int32_t* trow = table + (int64_t)b * max_blocks + lb0;
 
@@ -666,7 +681,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
       w.load(c, k_cache, v_cache, k_scale, v_scale, Hkv, g);
     };
 
-    w.load_q(q + ((int64_t)b * Hq + g * G) * D, G);
+    w.load_q(q, b, g, G, QL, Hq, ctx, window);
     w.reset();
     for (int j = j0; j < j1; j += U) {
       prep(cA, j);
@@ -676,23 +691,25 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
     w.reduce(l_w, ps_w);
     const bool whole = j0 == 0 && j1 == nv;
     const int64_t slot = (int64_t)b * Hkv + g + p;
+    const int ncol = G * QL;
 #pragma unroll
-    for (int h = 0; h < GP; ++h) {
+    for (int h = 0; h < GP; ++h) {  // column h: query row h / G, head g*G + h % G
       const float lh = __shfl(l_w, h), mh = __shfl(w.m_run, h);
-      if (h < G && w.ts == 0) {
+      if (h < ncol && w.ts == 0) {
         const float inv = lh > 0.f ? 1.0f / lh : 0.f;
         if (whole) {
           u32x4 o4;
 #pragma unroll
           for (int e = 0; e < 4; ++e) o4[e] = pack_bf16x2(w.acc[h][2 * e] * inv, w.acc[h][2 * e + 1] * inv);
-          *reinterpret_cast<u32x4*>(out + ((int64_t)b * Hq + g * G + h) * D + 8 * w.c8) = o4;
+          const int64_t orow = ((int64_t)b * QL + h / G) * Hq + g * G + h % G;
+          *reinterpret_cast<u32x4*>(out + orow * D + 8 * w.c8) = o4;
         } else {
-          float* po = part_o + ((slot * G + h) * D + 8 * w.c8);
+          float* po = part_o + ((slot * ncol + h) * D + 8 * w.c8);
           f32x4 a = {w.acc[h][0] * inv, w.acc[h][1] * inv, w.acc[h][2] * inv, w.acc[h][3] * inv};
           f32x4 c = {w.acc[h][4] * inv, w.acc[h][5] * inv, w.acc[h][6] * inv, w.acc[h][7] * inv};
           *reinterpret_cast<f32x4*>(po) = a;
           *reinterpret_cast<f32x4*>(po + 4) = c;
-          if (w.c8 == 0) part_lse[slot * G + h] = lh > 0.f ? mh + __log2f(lh) : -INFINITY;
+          if (w.c8 == 0) part_lse[slot * ncol + h] = lh > 0.f ? mh + __log2f(lh) : -INFINITY;
         }
       }
     }
@@ -706,16 +723,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
   }
 }
 
-// Merge for the balanced shape: (b, head h) gathers the pieces of segment (b, h / G) from
-// slots s + p0 .. s + p1; a segment held by one wave was written directly.
+// Merge for the balanced shape: column hl of KV head g of sequence b gathers the pieces of
+// segment s = (b, g) from slots s + p0 .. s + p1; a segment held by one wave was written
+// directly.
 template <int D>
 __global__ __launch_bounds__(64) void decode_stream_merge_kernel(
     const int32_t* __restrict__ prefix, const float* __restrict__ part_o,
     const float* __restrict__ part_lse, uint16_t* __restrict__ out, int B, int Hq, int Hkv,
-    int G, int P) {
-  const int h = blockIdx.x, b = blockIdx.y, g = h / G, hl = h % G;
+    int G, int QL, int P) {
+  const int ncol = G * QL;
+  const int g = blockIdx.x / ncol, hl = blockIdx.x % ncol, b = blockIdx.y;  // column hl of g
   const int nv = prefix[b + 1] - prefix[b];
-  uint16_t* orow = out + ((int64_t)b * Hq + h) * D;
+  uint16_t* orow = out + (((int64_t)b * QL + hl / G) * Hq + g * G + hl % G) * D;
   if (nv == 0) {  // empty context: zeros
 #pragma unroll
     for (int e = 0; e < D / 64; ++e) orow[threadIdx.x + 64 * e] = 0;
@@ -727,7 +746,7 @@ __global__ __launch_bounds__(64) void decode_stream_merge_kernel(
   const int64_t p0 = seg0 / qn, p1 = (seg0 + nv - 1) / qn;
   if (p0 == p1) return;
   const int64_t s = (int64_t)b * Hkv + g;
-  merge_partials<D>(part_o, part_lse, (s + p0) * G + hl, G, (int)(p1 - p0 + 1), orow);
+  merge_partials<D>(part_o, part_lse, (s + p0) * ncol + hl, ncol, (int)(p1 - p0 + 1), orow);
 }
 
 static int pow2_at_least(int g) {
@@ -749,10 +768,12 @@ static int device_cus() {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int max_context_len, int window,
+DecodePlan plan_decode(int B, int QL, int Hq, int Hkv, int D, int max_context_len, int window,
                        int split_tokens) {
   DecodePlan p{};
-  const int span = window > 0 ? std::min(max_context_len, window + 15) : max_context_len;
+  // keys the QL query rows of one sequence can attend to (block-rounded)
+  const int span = window > 0 ? std::min(max_context_len, window + QL - 1 + 15) : max_context_len;
+  const int ncol = (Hq / Hkv) * QL;  // query columns per (sequence, KV head)
   if (split_tokens == 0 && window == 0 && B <= kStreamMaxB) {
     // balanced shape (no window: context lengths, and so the work per sequence, can be
     // arbitrarily ragged): at most one wave per list entry, and no more waves than the GPU
@@ -762,11 +783,10 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int max_context_len, int w
     p.stream = true;
     p.stream_waves_max = (int)std::max<int64_t>(kDecodeWaves, waves);
     const size_t slots = (size_t)B * Hkv + p.stream_waves_max;
-    const int G = Hq / Hkv;
     p.prefix_off = 0;
     p.part_o_off = align256((size_t)(B + 1) * sizeof(int32_t));
-    p.part_lse_off = p.part_o_off + align256(slots * G * D * sizeof(float));
-    p.workspace_bytes = p.part_lse_off + slots * G * sizeof(float);
+    p.part_lse_off = p.part_o_off + align256(slots * ncol * D * sizeof(float));
+    p.workspace_bytes = p.part_lse_off + slots * ncol * sizeof(float);
     return p;
   }
   int C = split_tokens;
@@ -784,7 +804,7 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int max_context_len, int w
   if (p.n_split == 1) {
     p.workspace_bytes = 0;
   } else {
-    const size_t parts = (size_t)B * Hq * p.n_split;
+    const size_t parts = (size_t)B * Hkv * ncol * p.n_split;
     p.part_o_off = 0;
     p.part_lse_off = align256(parts * D * sizeof(float));
     p.workspace_bytes = p.part_lse_off + parts * sizeof(float);
@@ -808,10 +828,11 @@ static void launch_stream(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(kern, dim3(wgs), dim3(kDecodeThreads), 0, stream, (const uint16_t*)a.q,
                      a.k_cache, a.v_cache, (const __half*)a.k_scale, (const __half*)a.v_scale,
                      a.block_table, a.context_lens, (uint16_t*)a.o, prefix, part_o, part_lse, a.B,
-                     a.Hq, a.Hkv, G, a.max_blocks_per_seq, a.num_blocks, a.max_context_len,
-                     a.scale * kLog2e, a.window);
-  hipLaunchKernelGGL(decode_stream_merge_kernel<D>, dim3(a.Hq, a.B), dim3(64), 0, stream, prefix,
-                     part_o, part_lse, (uint16_t*)a.o, a.B, a.Hq, a.Hkv, G, wgs * kDecodeWaves);
+                     a.Hq, a.Hkv, G, a.q_len, a.max_blocks_per_seq, a.num_blocks,
+                     a.max_context_len, a.scale * kLog2e, a.window);
+  hipLaunchKernelGGL(decode_stream_merge_kernel<D>, dim3(a.Hkv * G * a.q_len, a.B), dim3(64), 0,
+                     stream, prefix, part_o, part_lse, (uint16_t*)a.o, a.B, a.Hq, a.Hkv, G,
+                     a.q_len, wgs * kDecodeWaves);
 }
 
 template <int D, int GP, bool I8>
@@ -824,13 +845,13 @@ static void launch_split(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((decode_split_kernel<D, GP, I8>), dim3(a.Hkv, a.B, ns), dim3(kDecodeThreads),
                      0, stream, (const uint16_t*)a.q, a.k_cache, a.v_cache,
                      (const __half*)a.k_scale, (const __half*)a.v_scale, a.block_table,
-                     a.context_lens, (uint16_t*)a.o, part_o, part_lse, a.Hq, a.Hkv, G,
+                     a.context_lens, (uint16_t*)a.o, part_o, part_lse, a.Hq, a.Hkv, G, a.q_len,
                      a.max_blocks_per_seq, a.num_blocks, a.max_context_len, a.scale * kLog2e,
                      a.window, C, ns);
   if (ns > 1)
-    hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(a.Hq, a.B), dim3(64), 0, stream, part_o,
-                       part_lse, a.context_lens, (uint16_t*)a.o, a.Hq, a.max_blocks_per_seq,
-                       a.max_context_len, a.window, C, ns);
+    hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(a.Hq, a.B * a.q_len), dim3(64), 0, stream,
+                       part_o, part_lse, a.context_lens, (uint16_t*)a.o, a.Hq, a.q_len,
+                       a.max_blocks_per_seq, a.max_context_len, a.window, C, ns);
 }
 
 template <int D, int GP, bool I8>
@@ -843,7 +864,7 @@ static void launch_shape(const DecodeArgs& a, hipStream_t stream) {
 
 template <int D, bool I8>
 static void launch_g(const DecodeArgs& a, hipStream_t stream) {
-  switch (pow2_at_least(a.Hq / a.Hkv)) {
+  switch (pow2_at_least(a.Hq / a.Hkv * a.q_len)) {  // MFMA columns: (query row, head) pairs
     case 1: launch_shape<D, 1, I8>(a, stream); break;
     case 2: launch_shape<D, 2, I8>(a, stream); break;
     case 4: launch_shape<D, 4, I8>(a, stream); break;

@@ -40,7 +40,7 @@ struct DecodeArgs {
   const int32_t* context_lens;
   void* o;
   bool int8;
-  int B, Hq, Hkv, D, block_size, max_blocks_per_seq, num_blocks, max_context_len;
+  int B, q_len, Hq, Hkv, D, block_size, max_blocks_per_seq, num_blocks, max_context_len;
   float scale;
   int window;
   DecodePlan plan;
@@ -77,7 +77,7 @@ struct PrefillPagedArgs {
   int causal, window;
 };
 
-DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int max_context_len, int window,
+DecodePlan plan_decode(int B, int q_len, int Hq, int Hkv, int D, int max_context_len, int window,
                        int split_tokens);
 
 int launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);

@@ -12,7 +12,8 @@ Each call is bracketed by HIP events on the stream the library launches on. The 
 timed steps; the decode HBM GB/s (algorithmic bytes: each visible K/V byte once, plus Q and O)
 is reported beside it. `--workload swa` / `int8_70b` time the other configurations the same way.
 Outside the timed steps, the default run also times attn_prefill_paged (chunked prefill over
-the paged cache with fused append: 4 sequences, 1024-token chunks after 3072-token prefixes).
+the paged cache with fused append: 4 sequences, 1024-token chunks after 3072-token prefixes)
+and attn_decode_paged_multi (4 draft rows per sequence on the decode cache).
 
 Prints one JSON line. Inputs are seeded synthetic tensors (synth/) resident in HBM before the
 timed region starts.
@@ -195,6 +196,41 @@ def time_chunked(t, A, reps: int):
                         "permuted pool"}
 
 
+def time_decode_multi(t, A, dwl, Dd, reps: int, q_len: int = 4):
+    """attn_decode_paged_multi (speculative verification, q_len draft rows per sequence) on the
+    decode workload's cache, timed per call with events after a cache-evicting read."""
+    from synth import new_tokens
+    qb, _ = new_tokens(dwl.seed + 91, dwl.B * q_len, dwl.Hq, dwl.D, "k")
+    q = _bf16(t, qb).view(dwl.B, q_len, dwl.Hq, dwl.D)
+    o = t.empty_like(q)
+    need = A.attn_decode_multi_workspace_size(dwl.B, q_len, dwl.Hq, dwl.Hkv, dwl.D, dwl.ctx_hi, dwl.window, 0)
+    ws = t.empty(max(need, 1), dtype=t.uint8, device="cuda")
+    flush = t.ones(512 * 1024 * 1024 // 4, dtype=t.float32, device="cuda")
+
+    def call():
+        A.attn_decode_paged_multi(q, Dd["kc"], Dd["vc"], Dd["table"], Dd["ctx"], dwl.ctx_hi,
+                                  k_scale=Dd["ks"], v_scale=Dd["vs"], scale=dwl.scale, window=dwl.window,
+                                  out=o, workspace=ws)
+    call()
+    ms = []
+    for _ in range(reps):
+        flush.sum()
+        e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        t.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    ms = float(np.mean(ms))
+    # algorithmic bytes: the visible K/V once (as single-token decode) plus q_len x Q and O
+    byts = decode_bytes(dwl, Dd["ctx_np"]) + 2.0 * dwl.B * (q_len - 1) * dwl.Hq * dwl.D * 2
+    gbs = byts / (ms * 1e-3) / 1e9
+    return {"kernel": "attn_decode_paged_multi", "q_len": q_len, "ms": ms, "GB/s": gbs,
+            "frac_hbm_peak": gbs / HBM_PEAK_GBS, "algorithmic_bytes": byts,
+            "tokens_per_s": dwl.B * q_len / (ms * 1e-3), "calls": reps,
+            "workload": f"{dwl.name} cache, {q_len} draft rows per sequence, causal among them"}
+
+
 def cpu_baseline(pwl, dwl, budget_s: float):
     """The oracle, untuned, on a time-bounded sample of the same workload."""
     import oracle
@@ -230,7 +266,7 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0 = skip)")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache-evicting scratch read")
     ap.add_argument("--no-chunked", action="store_true",
-                    help="skip the chunked paged prefill timing reported beside the step")
+                    help="skip the chunked-prefill and multi-row-decode timings reported beside the step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 3 times (counter calibration)")
     args = ap.parse_args(argv)
@@ -335,6 +371,7 @@ def main(argv=None):
                      "step": "kv_cache_append -> cache flush -> attn_decode_paged -> attn_prefill"}
     if args.workload == "llama1b" and not args.no_chunked:
         out["prefill_paged"] = time_chunked(t, A, max(5, args.steps))
+        out["decode_multi"] = time_decode_multi(t, A, dwl, Dd, max(5, args.steps))
     if args.cpu_budget > 0 and pwl is not None:
         out["cpu_baseline"] = cpu_baseline(pwl, dwl, args.cpu_budget)
     print(json.dumps(out), flush=True)

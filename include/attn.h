@@ -16,7 +16,8 @@
  *  [IL] "从零开始的LLM推理优化实验室：从PyTorch基线到Triton内核的完整实践",
  *       "KV缓存实验与长上下文优化": static, growing and sliding-window caches.
  *  [KD] "5 Fun Projects for LLM Inference Engineering" (KDnuggets), project 2 ("write your own
- *       FlashAttention kernel in Triton"): tiling and the online softmax cut HBM<->on-chip traffic.
+ *       FlashAttention kernel in Triton"): tiling and the online softmax cut HBM<->on-chip traffic;
+ *       project 4 (speculative decoding): the target model checks several draft tokens at once.
  *
  * Definition computed by every entry point (fp32 accumulation): for query row i of Sq rows
  * against Lk keys, its position is P = Lk - Sq + i; key j is visible iff (not causal or
@@ -152,6 +153,39 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       int block_size, int max_blocks_per_seq, int num_blocks,
                       int max_context_len, float scale, int window, int split_tokens,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_multi_workspace_size -- as attn_decode_workspace_size, for attn_decode_paged_multi
+ * with q_len query rows per sequence.
+ */
+size_t attn_decode_multi_workspace_size(int B, int q_len, int Hq, int Hkv, int D,
+                                        int max_context_len, int window, int split_tokens);
+
+/*
+ * attn_decode_paged_multi -- q_len new query rows per sequence against the paged cache: the
+ * verification step of speculative decoding, where the target model scores q_len draft tokens
+ * at once. [TI] "推测性解码与INT8量化" (a small draft model proposes tokens, the main model
+ * verifies them in parallel); [KD] project 4.
+ *
+ * Same arguments and rules as attn_decode_paged, except:
+ *  q, o         : [B][q_len][Hq][D] bf16. Row r of sequence b sits at position
+ *                 context_lens[b] - q_len + r and attends causally: to keys 0 .. that position
+ *                 (and, with a window, only the last `window` of them). The q_len draft tokens'
+ *                 K/V must already be in the cache (kv_cache_append), so context_lens counts
+ *                 them; rows whose position is negative produce zeros.
+ *  q_len        : >= 1, with (Hq / Hkv) * q_len <= 16 (ATTN_ERR_UNSUPPORTED above): the query
+ *                 heads of one KV head times the rows share one MFMA tile, so each K/V byte is
+ *                 still read once. Longer drafts: use attn_prefill_paged.
+ *  workspace    : at least attn_decode_multi_workspace_size(...) bytes.
+ * q_len == 1 computes exactly what attn_decode_paged computes.
+ */
+int attn_decode_paged_multi(const void* q, const void* k_cache, const void* v_cache,
+                            const void* k_scale, const void* v_scale,
+                            const int32_t* block_table, const int32_t* context_lens, void* o,
+                            int kv_dtype, int B, int q_len, int Hq, int Hkv, int D,
+                            int block_size, int max_blocks_per_seq, int num_blocks,
+                            int max_context_len, float scale, int window, int split_tokens,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * kv_cache_append -- write T new K/V rows into the paged cache.

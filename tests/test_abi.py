@@ -25,6 +25,7 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ("attn_prefill", "attn_decode_paged", "kv_cache_append", "attn_decode_workspace_size",
+              "attn_prefill_paged", "attn_decode_paged_multi", "attn_decode_multi_workspace_size",
               "attn_status_str", "attn_last_error"):
         assert n in names, n
 
@@ -88,6 +89,35 @@ def _decode(**kw):
 ])
 def test_decode_validation(kw, code):
     assert _decode(**kw) == code
+
+
+def _multi(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, ks=None, vs=None, table=FAKE, ctx=FAKE, o=FAKE,
+             kv=A.ATTN_BF16, B=2, ql=4, Hq=8, Hkv=2, D=64, bs=16, mb=4, nb=8, maxctx=64, scale=0.125,
+             window=0, split=0, ws=None, wsb=0)
+    a.update(kw)
+    return A.lib().attn_decode_paged_multi(a["q"], a["kc"], a["vc"], a["ks"], a["vs"], a["table"],
+                                           a["ctx"], a["o"], a["kv"], a["B"], a["ql"], a["Hq"], a["Hkv"],
+                                           a["D"], a["bs"], a["mb"], a["nb"], a["maxctx"], a["scale"],
+                                           a["window"], a["split"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), A.ATTN_ERR_NULL), (dict(ql=0), A.ATTN_ERR_SHAPE), (dict(ql=-1), A.ATTN_ERR_SHAPE),
+    (dict(ql=5), A.ATTN_ERR_UNSUPPORTED),               # 4 heads per KV head x 5 rows > 16
+    (dict(Hq=16, Hkv=1, ql=2), A.ATTN_ERR_UNSUPPORTED), (dict(B=40000), A.ATTN_ERR_SHAPE),
+    (dict(), A.ATTN_ERR_WORKSPACE),                     # the balanced shape stages partials
+])
+def test_decode_multi_validation(kw, code):
+    assert _multi(**kw) == code
+
+
+def test_multi_workspace_matches_single_row():
+    ws, wm = A.attn_decode_workspace_size, A.attn_decode_multi_workspace_size
+    for args in ((2, 8, 2, 64, 5000, 0, 64), (3, 32, 8, 128, 4096, 0, 0), (2, 8, 2, 64, 700, 100, 0)):
+        B, rest = args[0], args[1:]
+        assert wm(B, 1, *rest) == ws(B, *rest)
+    assert wm(3, 4, 32, 8, 128, 4096, 0, 0) > ws(3, 32, 8, 128, 4096, 0, 0)
 
 
 def test_workspace_size_rules():
