@@ -3,7 +3,8 @@
 Every computation runs in the HIP kernels of libattn.so; torch supplies device memory and the
 current stream. The names follow the C ABI in include/attn.h: attn_prefill,
 attn_prefill_paged, attn_decode_paged, attn_decode_paged_multi, kv_cache_append,
-attn_decode_workspace_size, attn_decode_multi_workspace_size.
+attn_decode_workspace_size, attn_decode_multi_workspace_size, kv_cache_append_rope,
+attn_rope_inplace.
 """
 from __future__ import annotations
 
@@ -32,6 +33,9 @@ _SIGS = {
     "attn_decode_paged_multi": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
                                      _I, _I, ctypes.c_float, _I, _I, _P, ctypes.c_size_t, _P]),
     "kv_cache_append": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
+    "kv_cache_append_rope": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
+                                  ctypes.c_float, _P]),
+    "attn_rope_inplace": (_I, [_P, _P, _I, _I, _I, ctypes.c_float, _P]),
     "attn_status_str": (ctypes.c_char_p, [_I]),
     "attn_last_error": (ctypes.c_char_p, []),
 }
@@ -199,3 +203,22 @@ def kv_cache_append(k_new, v_new, seq_idx, pos, block_table, k_cache, v_cache, *
         _ptr(k_new), _ptr(v_new), _ptr(seq_idx), _ptr(pos), _ptr(block_table), _ptr(k_cache),
         _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _dtype_code(k_cache), T, Hkv, D, bs,
         block_table.shape[0], block_table.shape[1], num_blocks, _stream(k_new)))
+
+
+def kv_cache_append_rope(k_new, v_new, seq_idx, pos, block_table, k_cache, v_cache, *,
+                         rope_base: float = 10000.0, k_scale=None, v_scale=None):
+    """kv_cache_append with each K row rotated (RoPE) at its position before it is stored."""
+    T, Hkv, D = k_new.shape
+    num_blocks, _, bs, _ = k_cache.shape
+    _check(lib().kv_cache_append_rope(
+        _ptr(k_new), _ptr(v_new), _ptr(seq_idx), _ptr(pos), _ptr(block_table), _ptr(k_cache),
+        _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _dtype_code(k_cache), T, Hkv, D, bs,
+        block_table.shape[0], block_table.shape[1], num_blocks, float(rope_base), _stream(k_new)))
+
+
+def attn_rope_inplace(x, pos, *, rope_base: float = 10000.0):
+    """Rotate bf16 rows x [T][H][D] in place at positions pos [T] (int32)."""
+    _need(x, "x")
+    T, H, D = x.shape
+    _check(lib().attn_rope_inplace(_ptr(x), _ptr(pos), T, H, D, float(rope_base), _stream(x)))
+    return x

@@ -6,27 +6,61 @@
 // from the table, slot inside the block). INT8 storage follows "推测性解码与INT8量化" there;
 // the scale rule (absmax / 127, fp16, symmetric, ties-to-even) is this library's reading.
 //
+// With RoPE (kv_cache_append_rope, attn_rope_inplace) the K rows are rotated first: rotary
+// position embedding applied where the rows already cross HBM, in the spirit of
+// "3.1 RMSNorm + RoPE 融合" on the triton-fused-ops page ("Triton融合算子优化：LLM推理性能提升3倍
+// 的工程实践"). The pages give no formula; this library takes the Llama convention: dimension
+// i < D/2 pairs with i + D/2 and the pair turns by pos * base^(-2i/D). The frequencies come
+// from an fp64 table built once per workgroup; the angle and its reduction modulo 2*pi are
+// fp64 (positions reach tens of thousands of radians); sin, cos and the rotation are fp32,
+// rounded to bf16 (RNE) when stored as bf16.
+//
 // HBM-bound elementwise work: one thread moves 8 elements (16 B of bf16 input); the D / 8
-// threads of one (token, head) row sit in adjacent lanes and reduce the row's absmax with
-// cross-lane shuffles. Division is IEEE (correctly rounded) so codes match a CPU reference
-// bit for bit.
+// threads of one (token, head) row sit in adjacent lanes and reduce the row's absmax (and
+// exchange RoPE partners) with cross-lane shuffles. Division is IEEE (correctly rounded) so
+// codes match a CPU reference bit for bit.
 #include "common.h"
 #include "launch.h"
 #include <hip/hip_fp16.h>
 
 namespace attn {
 
-// VARLEN: rows are a packed chunk (sequence b owns rows cu_q[b] .. cu_q[b+1]-1, the last
-// positions of its ctx[b] tokens) instead of explicit (seq_idx, pos) pairs.
-template <int D, bool I8, bool VARLEN>
+// inv_freq[i] = base^(-2i/D), i < D/2, in LDS
+template <int D>
+__device__ __forceinline__ void rope_table(double* inv_freq, double base) {
+  for (int i = threadIdx.x; i < D / 2; i += blockDim.x) inv_freq[i] = pow(base, -2.0 * i / D);
+  __syncthreads();
+}
+
+// Rotate the 8 values x (elements 8c .. 8c+7 of a D-wide row, c = lane's chunk) at position
+// pos. The partner half of the row sits TPR/2 lanes away; every lane of the row must call.
+template <int D>
+__device__ __forceinline__ void rope8(float (&x)[8], int c, int pos, const double* inv_freq) {
+  constexpr int TPR = D / 8;
+  constexpr double kTwoPi = 6.283185307179586476925286766559;
+  const bool lo_half = c < TPR / 2;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float y = __shfl_xor(x[e], TPR / 2, TPR);  // element d +- D/2
+    const double ang = (double)pos * inv_freq[(8 * c + e) % (D / 2)];
+    const float r = (float)(ang - kTwoPi * rint(ang * (1.0 / kTwoPi)));  // in [-pi, pi]
+    float sn, cs;
+    sincosf(r, &sn, &cs);
+    x[e] = lo_half ? fmaf(x[e], cs, -y * sn) : fmaf(y, sn, x[e] * cs);
+  }
+}
+
+template <int D, bool I8, bool VARLEN, bool ROPE>
 __global__ __launch_bounds__(256) void kv_append_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ table, void* __restrict__ k_cache, void* __restrict__ v_cache,
     __half* __restrict__ k_scale, __half* __restrict__ v_scale, int64_t rows, int Hkv, int bs,
     int num_seqs, int max_blocks, int num_blocks, const int32_t* __restrict__ cu_q,
-    const int32_t* __restrict__ ctx) {
+    const int32_t* __restrict__ ctx, double rope_base) {
   constexpr int TPR = D / 8;  // threads per (token, head) row
+  __shared__ double s_inv[ROPE ? D / 2 : 1];
+  if constexpr (ROPE) rope_table<D>(s_inv, rope_base);
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t row = gid / TPR;
   const int c = (int)(gid % TPR);
@@ -36,7 +70,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
   const int g = (int)(r % Hkv);
 
   bool valid = in_range;
-  int pb = 0, slot = 0;
+  int pb = 0, slot = 0, rpos = 0;
   if (valid) {
     int b, p;
     if constexpr (VARLEN) {
@@ -52,6 +86,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
       b = seq_idx[t];
       p = pos[t];
     }
+    rpos = p;
     valid = b >= 0 && b < num_seqs && p >= 0 && p < max_blocks * bs;
     if (valid) {
       pb = table[(int64_t)b * max_blocks + p / bs];
@@ -67,16 +102,22 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     const uint16_t* in = which == 0 ? k_new : v_new;
     u32x4 w = {0u, 0u, 0u, 0u};
     if (in_range) w = *reinterpret_cast<const u32x4*>(in + src);
+    const bool rot = ROPE && which == 0;  // RoPE turns K only
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16_lo(w[i]);
+      x[2 * i + 1] = bf16_hi(w[i]);
+    }
+    if (rot) rope8<D>(x, c, rpos, s_inv);
     if constexpr (!I8) {
       uint16_t* out = reinterpret_cast<uint16_t*>(which == 0 ? k_cache : v_cache);
+      if (rot) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+      }
       if (valid) *reinterpret_cast<u32x4*>(out + dst) = w;
     } else {
-      float x[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[2 * i] = bf16_lo(w[i]);
-        x[2 * i + 1] = bf16_hi(w[i]);
-      }
       float a = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));
@@ -107,9 +148,38 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
   }
 }
 
-template <bool VARLEN>
+// In-place RoPE of bf16 rows x [T][H][D] at positions pos[T] (the query side of the fused
+// append: Q is turned by the same rule before attention).
+template <int D>
+__global__ __launch_bounds__(256) void rope_rows_kernel(uint16_t* __restrict__ x,
+                                                        const int32_t* __restrict__ pos,
+                                                        int64_t rows, int H, double rope_base) {
+  constexpr int TPR = D / 8;
+  __shared__ double s_inv[D / 2];
+  rope_table<D>(s_inv, rope_base);
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = gid / TPR;
+  const int c = (int)(gid % TPR);
+  const bool in_range = row < rows;
+  const int64_t r = in_range ? row : 0;
+  u32x4 w = {0u, 0u, 0u, 0u};
+  uint16_t* p = x + r * D + 8 * c;
+  if (in_range) w = *reinterpret_cast<const u32x4*>(p);
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_lo(w[i]);
+    v[2 * i + 1] = bf16_hi(w[i]);
+  }
+  rope8<D>(v, c, in_range ? pos[r / H] : 0, s_inv);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+  if (in_range) *reinterpret_cast<u32x4*>(p) = w;
+}
+
+template <bool VARLEN, bool ROPE>
 static int launch_append(const AppendArgs& a, const int32_t* cu_q, const int32_t* ctx,
-                         hipStream_t stream) {
+                         double rope_base, hipStream_t stream) {
   const int64_t rows = (int64_t)a.T * a.Hkv;
   const int tpr = a.D / 8;
   const int64_t threads = rows * tpr;
@@ -117,11 +187,11 @@ static int launch_append(const AppendArgs& a, const int32_t* cu_q, const int32_t
   const int64_t grid = (threads + block - 1) / block;
   if (grid == 0) return 0;
 #define ATTN_APPEND(DD, I8)                                                                    \
-  hipLaunchKernelGGL((kv_append_kernel<DD, I8, VARLEN>), dim3((unsigned)grid), dim3(block), 0, \
-                     stream, (const uint16_t*)a.k_new, (const uint16_t*)a.v_new, a.seq_idx,    \
+  hipLaunchKernelGGL((kv_append_kernel<DD, I8, VARLEN, ROPE>), dim3((unsigned)grid), dim3(block), \
+                     0, stream, (const uint16_t*)a.k_new, (const uint16_t*)a.v_new, a.seq_idx,  \
                      a.pos, a.block_table, a.k_cache, a.v_cache, (__half*)a.k_scale,            \
                      (__half*)a.v_scale, rows, a.Hkv, a.block_size, a.num_seqs,                 \
-                     a.max_blocks_per_seq, a.num_blocks, cu_q, ctx)
+                     a.max_blocks_per_seq, a.num_blocks, cu_q, ctx, rope_base)
   if (a.D == 64) {
     if (a.int8) ATTN_APPEND(64, true); else ATTN_APPEND(64, false);
   } else {
@@ -132,12 +202,30 @@ static int launch_append(const AppendArgs& a, const int32_t* cu_q, const int32_t
 }
 
 int launch_kv_append(const AppendArgs& a, hipStream_t stream) {
-  return launch_append<false>(a, nullptr, nullptr, stream);
+  return launch_append<false, false>(a, nullptr, nullptr, 0.0, stream);
 }
 
 int launch_kv_append_varlen(const AppendArgs& a, const int32_t* cu_q, const int32_t* ctx,
                             hipStream_t stream) {
-  return launch_append<true>(a, cu_q, ctx, stream);
+  return launch_append<true, false>(a, cu_q, ctx, 0.0, stream);
+}
+
+int launch_kv_append_rope(const AppendArgs& a, double rope_base, hipStream_t stream) {
+  return launch_append<false, true>(a, nullptr, nullptr, rope_base, stream);
+}
+
+int launch_rope_rows(void* x, const int32_t* pos, int T, int H, int D, double rope_base,
+                     hipStream_t stream) {
+  const int64_t rows = (int64_t)T * H;
+  const int64_t grid = (rows * (D / 8) + 255) / 256;
+  if (grid == 0) return 0;
+  if (D == 64)
+    hipLaunchKernelGGL(rope_rows_kernel<64>, dim3((unsigned)grid), dim3(256), 0, stream,
+                       (uint16_t*)x, pos, rows, H, rope_base);
+  else
+    hipLaunchKernelGGL(rope_rows_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream,
+                       (uint16_t*)x, pos, rows, H, rope_base);
+  return 0;
 }
 
 }  // namespace attn

@@ -190,16 +190,19 @@ int attn_decode_paged_multi(const void* q, const void* k_cache, const void* v_ca
                      workspace, workspace_bytes, stream);
 }
 
-int kv_cache_append(const void* k_new, const void* v_new, const int32_t* seq_idx,
-                    const int32_t* pos, const int32_t* block_table, void* k_cache, void* v_cache,
-                    void* k_scale, void* v_scale, int cache_dtype, int T, int Hkv, int D,
-                    int block_size, int num_seqs, int max_blocks_per_seq, int num_blocks,
-                    void* stream) {
+static int append_impl(const char* who, const void* k_new, const void* v_new,
+                       const int32_t* seq_idx, const int32_t* pos, const int32_t* block_table,
+                       void* k_cache, void* v_cache, void* k_scale, void* v_scale,
+                       int cache_dtype, int T, int Hkv, int D, int block_size, int num_seqs,
+                       int max_blocks_per_seq, int num_blocks, bool rope, float rope_base,
+                       void* stream) {
   if (cache_dtype != ATTN_BF16 && cache_dtype != ATTN_I8)
     return fail(ATTN_ERR_DTYPE, "cache dtype %d", cache_dtype);
   if (T < 0) return fail(ATTN_ERR_SHAPE, "T %d < 0", T);
   if (Hkv < 1 || num_seqs < 1 || max_blocks_per_seq < 1 || num_blocks < 1)
     return fail(ATTN_ERR_SHAPE, "Hkv, num_seqs, max_blocks_per_seq, num_blocks must be >= 1");
+  if (rope && !(std::isfinite(rope_base) && rope_base > 0.f))
+    return fail(ATTN_ERR_SHAPE, "rope_base must be finite and > 0");
   if (!supported_d(D)) return fail(ATTN_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
   if (block_size != 16) return fail(ATTN_ERR_UNSUPPORTED, "block_size %d (supported: 16)", block_size);
   if ((long long)max_blocks_per_seq * block_size > 0x7fffffffLL)
@@ -212,8 +215,43 @@ int kv_cache_append(const void* k_new, const void* v_new, const int32_t* seq_idx
   attn::AppendArgs a{k_new, v_new, seq_idx, pos, block_table, k_cache, v_cache, k_scale, v_scale,
                      cache_dtype == ATTN_I8, T, Hkv, D, block_size, num_seqs, max_blocks_per_seq,
                      num_blocks};
-  attn::launch_kv_append(a, reinterpret_cast<hipStream_t>(stream));
-  return check_launch("kv_cache_append");
+  if (rope)
+    attn::launch_kv_append_rope(a, (double)rope_base, reinterpret_cast<hipStream_t>(stream));
+  else
+    attn::launch_kv_append(a, reinterpret_cast<hipStream_t>(stream));
+  return check_launch(who);
+}
+
+int kv_cache_append(const void* k_new, const void* v_new, const int32_t* seq_idx,
+                    const int32_t* pos, const int32_t* block_table, void* k_cache, void* v_cache,
+                    void* k_scale, void* v_scale, int cache_dtype, int T, int Hkv, int D,
+                    int block_size, int num_seqs, int max_blocks_per_seq, int num_blocks,
+                    void* stream) {
+  return append_impl("kv_cache_append", k_new, v_new, seq_idx, pos, block_table, k_cache, v_cache,
+                     k_scale, v_scale, cache_dtype, T, Hkv, D, block_size, num_seqs,
+                     max_blocks_per_seq, num_blocks, false, 0.f, stream);
+}
+
+int kv_cache_append_rope(const void* k_new, const void* v_new, const int32_t* seq_idx,
+                         const int32_t* pos, const int32_t* block_table, void* k_cache,
+                         void* v_cache, void* k_scale, void* v_scale, int cache_dtype, int T,
+                         int Hkv, int D, int block_size, int num_seqs, int max_blocks_per_seq,
+                         int num_blocks, float rope_base, void* stream) {
+  return append_impl("kv_cache_append_rope", k_new, v_new, seq_idx, pos, block_table, k_cache,
+                     v_cache, k_scale, v_scale, cache_dtype, T, Hkv, D, block_size, num_seqs,
+                     max_blocks_per_seq, num_blocks, true, rope_base, stream);
+}
+
+int attn_rope_inplace(void* x, const int32_t* pos, int T, int H, int D, float rope_base,
+                      void* stream) {
+  if (T < 0 || H < 1) return fail(ATTN_ERR_SHAPE, "T must be >= 0 and H >= 1");
+  if (!(std::isfinite(rope_base) && rope_base > 0.f))
+    return fail(ATTN_ERR_SHAPE, "rope_base must be finite and > 0");
+  if (!supported_d(D)) return fail(ATTN_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+  if (T == 0) return ok();
+  if (!x || !pos) return fail(ATTN_ERR_NULL, "x and pos are required");
+  attn::launch_rope_rows(x, pos, T, H, D, (double)rope_base, reinterpret_cast<hipStream_t>(stream));
+  return check_launch("attn_rope_inplace");
 }
 
 }  // extern "C"

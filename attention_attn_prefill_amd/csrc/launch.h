@@ -88,6 +88,9 @@ int launch_kv_append(const AppendArgs& a, hipStream_t stream);
 // position ctx[b] - (cu_q[b+1] - cu_q[b]) + (r - cu_q[b]). a.seq_idx / a.pos are unused.
 int launch_kv_append_varlen(const AppendArgs& a, const int32_t* cu_q, const int32_t* ctx,
                             hipStream_t stream);
+int launch_kv_append_rope(const AppendArgs& a, double rope_base, hipStream_t stream);
+int launch_rope_rows(void* x, const int32_t* pos, int T, int H, int D, double rope_base,
+                     hipStream_t stream);
 int launch_prefill_paged(const PrefillPagedArgs& a, hipStream_t stream);
 
 }  // namespace attn

@@ -13,7 +13,8 @@ timed steps; the decode HBM GB/s (algorithmic bytes: each visible K/V byte once,
 is reported beside it. `--workload swa` / `int8_70b` time the other configurations the same way.
 Outside the timed steps, the default run also times attn_prefill_paged (chunked prefill over
 the paged cache with fused append: 4 sequences, 1024-token chunks after 3072-token prefixes)
-and attn_decode_paged_multi (4 draft rows per sequence on the decode cache).
+attn_decode_paged_multi (4 draft rows per sequence on the decode cache) and
+kv_cache_append_rope (a 64k-token prompt written into a paged cache with RoPE on K).
 
 Prints one JSON line. Inputs are seeded synthetic tensors (synth/) resident in HBM before the
 timed region starts.
@@ -231,6 +232,40 @@ def time_decode_multi(t, A, dwl, Dd, reps: int, q_len: int = 4):
             "workload": f"{dwl.name} cache, {q_len} draft rows per sequence, causal among them"}
 
 
+def time_append_rope(t, A, reps: int):
+    """kv_cache_append_rope filling a permuted bf16 cache with 16 x 4096 prompt tokens (8 KV
+    heads, D = 128): HBM GB/s of the rows read and written."""
+    from synth import paged_table
+    B, S, Hkv, D = 16, 4096, 8, 128
+    ctx = np.full(B, S, np.int32)
+    table, nb = paged_table(ctx, 16, 1404)
+    T = B * S
+    gen = t.Generator(device="cuda").manual_seed(1404)
+    kn = t.randn((T, Hkv, D), device="cuda", generator=gen).to(t.bfloat16)
+    vn = t.randn((T, Hkv, D), device="cuda", generator=gen).to(t.bfloat16)
+    seq = t.arange(B, dtype=t.int32, device="cuda").repeat_interleave(S)
+    pos = t.arange(S, dtype=t.int32, device="cuda").repeat(B)
+    kc = t.empty((nb, Hkv, 16, D), dtype=t.bfloat16, device="cuda")
+    vc = t.empty_like(kc)
+    tt = t.from_numpy(table).cuda()
+
+    def call():
+        A.kv_cache_append_rope(kn, vn, seq, pos, tt, kc, vc, rope_base=500000.0)
+    call()
+    ev = [(t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        call()
+        e1.record()
+    t.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    byts = 4.0 * T * Hkv * D * 2 + 2.0 * T * 4  # K, V read and written; seq, pos read
+    gbs = byts / (ms * 1e-3) / 1e9
+    return {"kernel": "kv_cache_append_rope", "ms": ms, "GB/s": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS,
+            "algorithmic_bytes": byts, "calls": reps,
+            "workload": f"{T} tokens ({B} x {S}), Hkv={Hkv} D={D} bf16, RoPE base 500000, permuted pool"}
+
+
 def cpu_baseline(pwl, dwl, budget_s: float):
     """The oracle, untuned, on a time-bounded sample of the same workload."""
     import oracle
@@ -372,6 +407,7 @@ def main(argv=None):
     if args.workload == "llama1b" and not args.no_chunked:
         out["prefill_paged"] = time_chunked(t, A, max(5, args.steps))
         out["decode_multi"] = time_decode_multi(t, A, dwl, Dd, max(5, args.steps))
+        out["append_rope"] = time_append_rope(t, A, max(5, args.steps))
     if args.cpu_budget > 0 and pwl is not None:
         out["cpu_baseline"] = cpu_baseline(pwl, dwl, args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -15,6 +15,9 @@
  *         changed to run incrementally (one new token against the cache) for decode.
  *  [IL] "从零开始的LLM推理优化实验室：从PyTorch基线到Triton内核的完整实践",
  *       "KV缓存实验与长上下文优化": static, growing and sliding-window caches.
+ *  [TF] "Triton融合算子优化：LLM推理性能提升3倍的工程实践", "3.1 RMSNorm + RoPE 融合": rotary
+ *       position embedding applied at the rows' position ids inside a neighbouring
+ *       elementwise kernel, so the rows cross HBM once.
  *  [KD] "5 Fun Projects for LLM Inference Engineering" (KDnuggets), project 2 ("write your own
  *       FlashAttention kernel in Triton"): tiling and the online softmax cut HBM<->on-chip traffic;
  *       project 4 (speculative decoding): the target model checks several draft tokens at once.
@@ -211,6 +214,34 @@ int kv_cache_append(const void* k_new, const void* v_new, const int32_t* seq_idx
                     void* k_cache, void* v_cache, void* k_scale, void* v_scale,
                     int cache_dtype, int T, int Hkv, int D, int block_size,
                     int num_seqs, int max_blocks_per_seq, int num_blocks, void* stream);
+
+/*
+ * kv_cache_append_rope -- kv_cache_append with rotary position embedding fused into the write:
+ * each K row is turned at its own position pos[t] before it is stored (and quantized, for an
+ * INT8 cache); V rows are stored as in kv_cache_append. [TF] "3.1 RMSNorm + RoPE 融合"; [TI]
+ * "技术架构与模块设计" (RoPE among the Llama 3.2 1B operators).
+ * RoPE rule (the pages name it without a formula; Llama convention): for i < D/2, element i
+ * pairs with element i + D/2 and the pair is rotated by the angle pos * rope_base^(-2i/D):
+ *   out_i = x_i cos - x_{i+D/2} sin,  out_{i+D/2} = x_i sin + x_{i+D/2} cos,
+ * the angle in fp64 (reduced modulo 2*pi in fp64), sin, cos and the rotation in fp32, the
+ * result rounded to bf16 (nearest even) for a bf16 cache. rope_base: finite and > 0 (Llama 3.2 uses 500000, the original
+ * RoPE 10000); otherwise ATTN_ERR_SHAPE. Everything else as kv_cache_append.
+ */
+int kv_cache_append_rope(const void* k_new, const void* v_new, const int32_t* seq_idx,
+                         const int32_t* pos, const int32_t* block_table,
+                         void* k_cache, void* v_cache, void* k_scale, void* v_scale,
+                         int cache_dtype, int T, int Hkv, int D, int block_size,
+                         int num_seqs, int max_blocks_per_seq, int num_blocks, float rope_base,
+                         void* stream);
+
+/*
+ * attn_rope_inplace -- the same rotation applied in place to bf16 rows x [T][H][D] at
+ * positions pos[T] (int32): the query side, turned before attention by the rule the cache
+ * append used for K. [TF] "3.1 RMSNorm + RoPE 融合".
+ * Requirements: T >= 0 (0 = no-op), H >= 1, D in {64, 128}, rope_base finite and > 0.
+ */
+int attn_rope_inplace(void* x, const int32_t* pos, int T, int H, int D, float rope_base,
+                      void* stream);
 
 /* Static string naming a status code. */
 const char* attn_status_str(int status);

@@ -16,6 +16,10 @@ What the pages fix, and where (page title, section):
        - 推测性解码与INT8量化: the KV cache is stored as INT8 instead of FP16.
   [IL] "从零开始的LLM推理优化实验室：从PyTorch基线到Triton内核的完整实践", KV缓存实验与长上下文优化:
        static, growing and sliding-window KV caches.
+  [TF] "Triton融合算子优化：LLM推理性能提升3倍的工程实践", 3.1 RMSNorm + RoPE 融合: rotary
+       position embedding applied to rows at their position ids, fused with the neighbouring
+       elementwise step so the rows cross HBM once; [TI] 技术架构与模块设计 lists RoPE among the
+       Llama 3.2 1B operators.
 
 Readings where the pages are silent (the same list is kept in the design notes):
   * query i of Sq queries against Lk keys sits at absolute position P(i) = Lk - Sq + i
@@ -28,7 +32,10 @@ Readings where the pages are silent (the same list is kept in the design notes):
   * INT8 KV: per token and KV head, a = max|x|, s = fp16(fp32(a) / 127) (both roundings to
     nearest-even), code = clamp(rint(fp32(x) / fp32(s)), -127, 127) with rint ties-to-even;
     s == 0 (a == 0, or a / 127 below half the smallest fp16 subnormal) gives code 0; the
-    dequantized value the attention sees is code * s, exactly.
+    dequantized value the attention sees is code * s, exactly;
+  * RoPE (the pages name it, give no formula): the Llama convention -- dimension i < D/2 is
+    paired with i + D/2 and the pair is rotated by the angle pos * base^(-2i/D); the rotated
+    fp64 value is rounded to fp32 and then to bf16 (both to nearest-even) when stored as bf16.
 
 Every function computes in float64 from the exact values the GPU receives.
 """
@@ -37,7 +44,8 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "visible_mask", "attention_head", "attention", "gather_logical", "decode_paged",
+    "visible_mask", "attention_head", "attention", "gather_logical", "decode_paged", "rope",
+    "bf16_round",
     "prefill_paged", "quantize_int8", "dequantize_int8", "append_expected", "merge_partials",
 ]
 
@@ -212,6 +220,30 @@ def append_expected(pool, rows, seq_idx, pos, table, block_size: int):
         pb = int(table[b][p // block_size])
         out[pb, :, p % block_size] = rows[t]
     return out
+
+
+def rope(x, pos, base: float = 10000.0):
+    """Rotary position embedding of rows x [T][H][D] (any float) at positions pos [T], fp64.
+
+    Pair (i, i + D/2) of row t is rotated by angle pos[t] * base ** (-2 i / D):
+    out_i = x_i cos - x_{i+D/2} sin, out_{i+D/2} = x_i sin + x_{i+D/2} cos.
+    """
+    x = np.asarray(x, np.float64)
+    D = x.shape[-1]
+    half = D // 2
+    inv_freq = base ** (-2.0 * np.arange(half) / D)
+    ang = np.asarray(pos, np.float64)[:, None] * inv_freq[None, :]  # [T][D/2]
+    c, s_ = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    a, b = x[..., :half], x[..., half:]
+    return np.concatenate([a * c - b * s_, a * s_ + b * c], axis=-1)
+
+
+def bf16_round(x):
+    """fp64 -> fp32 -> bf16 (each to nearest-even), returned as the bf16 values in float64."""
+    f = np.asarray(x, np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
 def merge_partials(outs, lses):

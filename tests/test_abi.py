@@ -170,3 +170,26 @@ def _paged(**kw):
 ])
 def test_prefill_paged_validation(kw, code):
     assert _paged(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(base=0.0), A.ATTN_ERR_SHAPE), (dict(base=float("nan")), A.ATTN_ERR_SHAPE),
+    (dict(base=-5.0), A.ATTN_ERR_SHAPE), (dict(D=96), A.ATTN_ERR_UNSUPPORTED),
+    (dict(kn=None), A.ATTN_ERR_NULL), (dict(T=0, kn=None), A.ATTN_OK),
+])
+def test_append_rope_validation(kw, code):
+    a = dict(kn=FAKE, T=4, D=64, base=10000.0)
+    a.update(kw)
+    r = A.lib().kv_cache_append_rope(a["kn"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                                     A.ATTN_BF16, a["T"], 2, a["D"], 16, 2, 4, 8, a["base"], None)
+    assert r == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=0), A.ATTN_ERR_SHAPE), (dict(T=-1), A.ATTN_ERR_SHAPE), (dict(D=32), A.ATTN_ERR_UNSUPPORTED),
+    (dict(base=0.0), A.ATTN_ERR_SHAPE), (dict(x=None), A.ATTN_ERR_NULL), (dict(T=0, x=None), A.ATTN_OK),
+])
+def test_rope_inplace_validation(kw, code):
+    a = dict(x=FAKE, T=3, H=2, D=64, base=10000.0)
+    a.update(kw)
+    assert A.lib().attn_rope_inplace(a["x"], FAKE, a["T"], a["H"], a["D"], a["base"], None) == code

@@ -474,3 +474,57 @@ def test_prefill_paged_single_row_is_decode():
     od, _ = oracle.decode_paged(q, kp, vp, table, ctx, 0.3, bs, 2)
     op, _ = oracle.prefill_paged(q, np.arange(4), kp, vp, table, ctx, 0.3, bs, True, 2)
     assert np.abs(od - op).max() < 1e-14
+
+
+# ---- RoPE (rotary position embedding; Llama pairing (i, i + D/2), theta_i = base^(-2i/D)) ----
+def test_rope_identity_at_position_zero():
+    x = np.random.default_rng(0).standard_normal((3, 2, 64))
+    assert np.array_equal(oracle.rope(x, [0, 0, 0]), x)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_rope_basis_vectors_closed_form(D):
+    """Hand-computed rotations pin the pairing and the frequency schedule: e_0 turns by the
+    angle pos (theta_0 = 1) into e_{D/2}; e_{D/4} has theta = base^(-1/2), so with base 10^4 it
+    turns by 1 rad at pos 100, into e_{3D/4}; e_{D/2} turns back towards -e_0."""
+    e = np.eye(D)
+    out = oracle.rope(e[None, [0]], [3], 10000.0)[0, 0]
+    want = np.zeros(D)
+    want[0], want[D // 2] = math.cos(3.0), math.sin(3.0)
+    assert np.allclose(out, want, atol=1e-15)
+    out = oracle.rope(e[None, [D // 4]], [100], 10000.0)[0, 0]
+    want = np.zeros(D)
+    want[D // 4], want[3 * D // 4] = math.cos(1.0), math.sin(1.0)
+    assert np.allclose(out, want, atol=1e-12)
+    out = oracle.rope(e[None, [D // 2]], [3], 10000.0)[0, 0]
+    want = np.zeros(D)
+    want[0], want[D // 2] = -math.sin(3.0), math.cos(3.0)
+    assert np.allclose(out, want, atol=1e-15)
+
+
+def test_rope_group_norm_and_relative_position():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((4, 3, 64))
+    a, b = np.array([0, 5, 77, 4000]), np.array([1, 9, 300, 12345])
+    # composition: turning by a then by b is turning by a + b
+    assert np.allclose(oracle.rope(oracle.rope(x, a), b), oracle.rope(x, a + b), atol=1e-9)
+    # each (i, i + D/2) pair keeps its length
+    r = oracle.rope(x, b)
+    n0 = x[..., :32] ** 2 + x[..., 32:] ** 2
+    n1 = r[..., :32] ** 2 + r[..., 32:] ** 2
+    assert np.allclose(n0, n1, atol=1e-12)
+    # q.k after rotation depends only on the position difference
+    q, k = rng.standard_normal((1, 1, 64)), rng.standard_normal((1, 1, 64))
+    d1 = (oracle.rope(q, [50]) * oracle.rope(k, [20])).sum()
+    d2 = (oracle.rope(q, [1030]) * oracle.rope(k, [1000])).sum()
+    assert abs(d1 - d2) < 1e-9
+
+
+def test_bf16_round_hand_values():
+    ulp = 2.0 ** -7  # bf16 spacing in [1, 2)
+    vals = np.array([1.0, 1 + ulp / 2, 1 + 1.5 * ulp, 1 + ulp / 2 + 2.0 ** -20, -3.0, 0.0])
+    want = np.array([1.0, 1.0, 1 + 2 * ulp, 1 + ulp, -3.0, 0.0])
+    assert np.array_equal(oracle.bf16_round(vals), want)
+    # the rounding agrees with the bit-level generator's on random fp32 values
+    x = np.random.default_rng(2).standard_normal(1000).astype(np.float32)
+    assert np.array_equal(oracle.bf16_round(x), bf16_value(bf16_bits(x)))
