@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(HERE, "libattn.so")
 
 ATTN_OK, ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_DTYPE, ATTN_ERR_UNSUPPORTED, \
     ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(7)
-ATTN_F32, ATTN_BF16, ATTN_I8 = 0, 1, 2
+ATTN_F32, ATTN_BF16, ATTN_I8, ATTN_FP8 = 0, 1, 2, 3
 
 _lib = None
 
@@ -86,6 +86,8 @@ def _dtype_code(t):
         return ATTN_BF16
     if t.dtype == torch.int8:
         return ATTN_I8
+    if t.dtype == torch.uint8 or t.dtype == getattr(torch, "float8_e4m3fn", None):
+        return ATTN_FP8  # FP8 E4M3 codes, one per byte
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -143,8 +145,8 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, max_contex
                       split_tokens: int = 0, out=None, workspace=None):
     """Single-token decode over a paged cache.
 
-    q [B][Hq][D] bf16; caches [num_blocks][Hkv][block_size][D] bf16 or int8 (+ fp16 scales
-    [num_blocks][Hkv][block_size]); block_table int32 [B][max_blocks]; context_lens int32 [B].
+    q [B][Hq][D] bf16; caches [num_blocks][Hkv][block_size][D] bf16, int8, or uint8 /
+    float8_e4m3fn holding FP8 E4M3 codes (+ fp16 scales [num_blocks][Hkv][block_size]); block_table int32 [B][max_blocks]; context_lens int32 [B].
     A workspace of attn_decode_workspace_size(...) bytes is allocated when not given.
     """
     import torch

@@ -1,10 +1,12 @@
 // kv_cache_append: write new K/V rows into a paged cache, copying bf16 bits or quantizing to
-// INT8 with a per-(token, KV head) fp16 scale.
+// INT8 or FP8 E4M3 with a per-(token, KV head) fp16 scale.
 //
 // Paged placement follows "分页KV缓存：借鉴操作系统的内存管理" on the Tiny-Infer page
 // ("从零构建CUDA推理引擎：Tiny-Infer项目的技术深度解析"): logical position -> (physical block
 // from the table, slot inside the block). INT8 storage follows "推测性解码与INT8量化" there;
-// the scale rule (absmax / 127, fp16, symmetric, ties-to-even) is this library's reading.
+// FP8 E4M3 with a dynamic per-token scale follows "3.3 FP8量化支持" on the triton-fused-ops
+// page. The scale rule (absmax / 127 or / 448, fp16, symmetric, ties-to-even) is this
+// library's reading.
 //
 // With RoPE (kv_cache_append_rope, attn_rope_inplace) the K rows are rotated first: rotary
 // position embedding applied where the rows already cross HBM, in the spirit of
@@ -50,7 +52,7 @@ __device__ __forceinline__ void rope8(float (&x)[8], int c, int pos, const doubl
   }
 }
 
-template <int D, bool I8, bool VARLEN, bool ROPE>
+template <int D, int KV, bool VARLEN, bool ROPE>
 __global__ __launch_bounds__(256) void kv_append_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
       x[2 * i + 1] = bf16_hi(w[i]);
     }
     if (rot) rope8<D>(x, c, rpos, s_inv);
-    if constexpr (!I8) {
+    if constexpr (KV == kKvBf16) {
       uint16_t* out = reinterpret_cast<uint16_t*>(which == 0 ? k_cache : v_cache);
       if (rot) {
 #pragma unroll
@@ -123,21 +125,33 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
       for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));
 #pragma unroll
       for (int m = 1; m < TPR; m <<= 1) a = fmaxf(a, __shfl_xor(a, m, TPR));
-      const float s32 = __fdiv_rn(a, 127.0f);
+      constexpr float kMaxCode = KV == kKvI8 ? 127.0f : 448.0f;  // INT8 / FP8 E4M3 largest
+      const float s32 = __fdiv_rn(a, kMaxCode);
       const __half s16 = __float2half_rn(s32);
       const float sf = __half2float(s16);
       uint32_t packed[2] = {0u, 0u};
+      if constexpr (KV == kKvI8) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        int code = 0;
-        if (sf != 0.0f) {
-          float qv = rintf(__fdiv_rn(x[i], sf));
-          qv = fminf(fmaxf(qv, -127.0f), 127.0f);
-          code = (int)qv;
+        for (int i = 0; i < 8; ++i) {
+          int code = 0;
+          if (sf != 0.0f) {
+            float qv = rintf(__fdiv_rn(x[i], sf));
+            qv = fminf(fmaxf(qv, -127.0f), 127.0f);
+            code = (int)qv;
+          }
+          packed[i / 4] |= ((uint32_t)code & 0xffu) << (8 * (i % 4));
         }
-        packed[i / 4] |= ((uint32_t)code & 0xffu) << (8 * (i % 4));
+      } else if (sf != 0.0f) {
+        // E4M3 of the clamped quotient, round to nearest even, by the hardware conversion
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          const float y0 = fminf(fmaxf(__fdiv_rn(x[i], sf), -448.0f), 448.0f);
+          const float y1 = fminf(fmaxf(__fdiv_rn(x[i + 1], sf), -448.0f), 448.0f);
+          const uint32_t two = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false) & 0xffffu;
+          packed[i / 4] |= two << (8 * (i % 4));
+        }
       }
-      int8_t* out = reinterpret_cast<int8_t*>(which == 0 ? k_cache : v_cache);
+      uint8_t* out = reinterpret_cast<uint8_t*>(which == 0 ? k_cache : v_cache);
       __half* sc = which == 0 ? k_scale : v_scale;
       if (valid) {
         u32x2 pk = {packed[0], packed[1]};
@@ -186,16 +200,16 @@ static int launch_append(const AppendArgs& a, const int32_t* cu_q, const int32_t
   const int block = 256;
   const int64_t grid = (threads + block - 1) / block;
   if (grid == 0) return 0;
-#define ATTN_APPEND(DD, I8)                                                                    \
-  hipLaunchKernelGGL((kv_append_kernel<DD, I8, VARLEN, ROPE>), dim3((unsigned)grid), dim3(block), \
+#define ATTN_APPEND(DD, KV)                                                                    \
+  hipLaunchKernelGGL((kv_append_kernel<DD, KV, VARLEN, ROPE>), dim3((unsigned)grid), dim3(block), \
                      0, stream, (const uint16_t*)a.k_new, (const uint16_t*)a.v_new, a.seq_idx,  \
                      a.pos, a.block_table, a.k_cache, a.v_cache, (__half*)a.k_scale,            \
                      (__half*)a.v_scale, rows, a.Hkv, a.block_size, a.num_seqs,                 \
                      a.max_blocks_per_seq, a.num_blocks, cu_q, ctx, rope_base)
   if (a.D == 64) {
-    if (a.int8) ATTN_APPEND(64, true); else ATTN_APPEND(64, false);
+    if (a.kv == kKvI8) ATTN_APPEND(64, kKvI8); else if (a.kv == kKvFp8) ATTN_APPEND(64, kKvFp8); else ATTN_APPEND(64, kKvBf16);
   } else {
-    if (a.int8) ATTN_APPEND(128, true); else ATTN_APPEND(128, false);
+    if (a.kv == kKvI8) ATTN_APPEND(128, kKvI8); else if (a.kv == kKvFp8) ATTN_APPEND(128, kKvFp8); else ATTN_APPEND(128, kKvBf16);
   }
 #undef ATTN_APPEND
   return 0;

@@ -37,6 +37,10 @@ int check_launch(const char* what) {
 
 bool supported_d(int D) { return D == 64 || D == 128; }
 
+int kv_kind(int dtype) {
+  return dtype == ATTN_I8 ? attn::kKvI8 : dtype == ATTN_FP8 ? attn::kKvFp8 : attn::kKvBf16;
+}
+
 }  // namespace
 
 extern "C" {
@@ -132,10 +136,10 @@ static int decode_impl(const char* who, const void* q, const void* k_cache, cons
                        int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k_cache || !v_cache || !block_table || !context_lens || !o)
     return fail(ATTN_ERR_NULL, "q, k_cache, v_cache, block_table, context_lens and o are required");
-  if (kv_dtype != ATTN_BF16 && kv_dtype != ATTN_I8)
+  if (kv_dtype != ATTN_BF16 && kv_dtype != ATTN_I8 && kv_dtype != ATTN_FP8)
     return fail(ATTN_ERR_DTYPE, "decode kv_dtype %d", kv_dtype);
-  if (kv_dtype == ATTN_I8 && (!k_scale || !v_scale))
-    return fail(ATTN_ERR_NULL, "int8 cache needs k_scale and v_scale");
+  if (kv_dtype != ATTN_BF16 && (!k_scale || !v_scale))
+    return fail(ATTN_ERR_NULL, "an int8 / fp8 cache needs k_scale and v_scale");
   if (kv_dtype == ATTN_BF16 && (k_scale || v_scale))
     return fail(ATTN_ERR_SHAPE, "k_scale/v_scale must be NULL for a bf16 cache");
   if (B < 1 || q_len < 1 || Hq < 1 || Hkv < 1 || max_blocks_per_seq < 1 || num_blocks < 1 ||
@@ -159,7 +163,7 @@ static int decode_impl(const char* who, const void* q, const void* k_cache, cons
     return fail(ATTN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", plan.workspace_bytes,
                 workspace ? workspace_bytes : (size_t)0);
   attn::DecodeArgs a{q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, o,
-                     kv_dtype == ATTN_I8, B, q_len, Hq, Hkv, D, block_size, max_blocks_per_seq,
+                     kv_kind(kv_dtype), B, q_len, Hq, Hkv, D, block_size, max_blocks_per_seq,
                      num_blocks, max_context_len, scale, window, plan, workspace};
   attn::launch_decode(a, reinterpret_cast<hipStream_t>(stream));
   return check_launch(who);
@@ -196,7 +200,7 @@ static int append_impl(const char* who, const void* k_new, const void* v_new,
                        int cache_dtype, int T, int Hkv, int D, int block_size, int num_seqs,
                        int max_blocks_per_seq, int num_blocks, bool rope, float rope_base,
                        void* stream) {
-  if (cache_dtype != ATTN_BF16 && cache_dtype != ATTN_I8)
+  if (cache_dtype != ATTN_BF16 && cache_dtype != ATTN_I8 && cache_dtype != ATTN_FP8)
     return fail(ATTN_ERR_DTYPE, "cache dtype %d", cache_dtype);
   if (T < 0) return fail(ATTN_ERR_SHAPE, "T %d < 0", T);
   if (Hkv < 1 || num_seqs < 1 || max_blocks_per_seq < 1 || num_blocks < 1)
@@ -210,10 +214,10 @@ static int append_impl(const char* who, const void* k_new, const void* v_new,
   if (T == 0) return ok();
   if (!k_new || !v_new || !seq_idx || !pos || !block_table || !k_cache || !v_cache)
     return fail(ATTN_ERR_NULL, "k_new, v_new, seq_idx, pos, block_table, k_cache, v_cache are required");
-  if (cache_dtype == ATTN_I8 && (!k_scale || !v_scale))
-    return fail(ATTN_ERR_NULL, "int8 cache needs k_scale and v_scale");
+  if (cache_dtype != ATTN_BF16 && (!k_scale || !v_scale))
+    return fail(ATTN_ERR_NULL, "an int8 / fp8 cache needs k_scale and v_scale");
   attn::AppendArgs a{k_new, v_new, seq_idx, pos, block_table, k_cache, v_cache, k_scale, v_scale,
-                     cache_dtype == ATTN_I8, T, Hkv, D, block_size, num_seqs, max_blocks_per_seq,
+                     kv_kind(cache_dtype), T, Hkv, D, block_size, num_seqs, max_blocks_per_seq,
                      num_blocks};
   if (rope)
     attn::launch_kv_append_rope(a, (double)rope_base, reinterpret_cast<hipStream_t>(stream));

@@ -68,6 +68,18 @@ __device__ __forceinline__ uint32_t widen_lo(uint32_t u) { return __builtin_amdg
 __device__ __forceinline__ uint32_t widen_hi(uint32_t u) { return __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u); }
 constexpr float kI8Bias = 1152.0f;
 
+// FP8 E4M3 -> fp16 without conversions: for a code c, the fp16 bit pattern
+// ((c & 0x7f) << 7) | ((c & 0x80) << 8) is exactly value(c) * 2^-8 (the 4-bit exponent with bias
+// 7 lands in fp16's 5-bit exponent with bias 15, subnormals included; NaN codes are never
+// stored). fp8x2_lo / fp8x2_hi turn bytes 0, 1 / 2, 3 of u into an fp16 pair; the 2^8 is put
+// back on the scores and the accumulators.
+__device__ __forceinline__ uint32_t fp8x2(uint32_t v) {  // v: bytes at bits 0-7 and 16-23
+  return ((v & 0x007f007fu) << 7) | ((v & 0x00800080u) << 8);
+}
+__device__ __forceinline__ uint32_t fp8x2_lo(uint32_t u) { return fp8x2(__builtin_amdgcn_perm(0u, u, 0x0c010c00u)); }
+__device__ __forceinline__ uint32_t fp8x2_hi(uint32_t u) { return fp8x2(__builtin_amdgcn_perm(0u, u, 0x0c030c02u)); }
+constexpr float kF8Unscale = 256.0f;
+
 // xor-16 / xor-32 lane partners within a wave
 __device__ __forceinline__ float max_x32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -82,13 +94,14 @@ __device__ __forceinline__ float sum_x32(float x) {
 // bf16 D=64) are the unit of work of one wave: their K and V loads are all issued before any of
 // them is consumed. Small chunks keep register use low, so more waves stay resident and more
 // bytes are in flight per CU (measured better than larger per-wave batches).
-template <int D, bool I8>
+template <int D, int KV>
 struct DecodeShape {
+  static constexpr bool BYTE = KV != kKvBf16;              // one byte per cached element
   static constexpr int BS = 16;
-  static constexpr int U = (D == 64 || I8) ? 2 : 1;       // blocks per chunk
+  static constexpr int U = (D == 64 || BYTE) ? 2 : 1;     // blocks per chunk
   static constexpr int KSTEPS = D / 32;                    // MFMA k-steps per block
-  static constexpr int KLOADS = I8 ? D / 64 : D / 32;      // 16-byte K loads per lane per block
-  static constexpr int VBYTES = I8 ? 8 : 16;               // bytes per lane per V load (8 elements)
+  static constexpr int KLOADS = BYTE ? D / 64 : D / 32;    // 16-byte K loads per lane per block
+  static constexpr int VBYTES = BYTE ? 8 : 16;             // bytes per lane per V load (8 elements)
   static constexpr int CPR = D / 8;                        // lanes per V row
   static constexpr int TPW = 64 / CPR;                     // tokens per V load instruction
   static constexpr int VLOADS = BS / TPW;                  // V loads per lane per block
@@ -96,17 +109,18 @@ struct DecodeShape {
 
 // Per-wave decode state: Q fragments, running max, row-sum shares and PV accumulators of the
 // G heads of one (sequence, KV head). The LDS staging slices belong to the wave.
-template <int D, int GP, bool I8>
+template <int D, int GP, int KV>
 struct DecodeWave {
-  using SH = DecodeShape<D, I8>;
+  using SH = DecodeShape<D, KV>;
+  static constexpr bool BYTE = SH::BYTE, I8 = KV == kKvI8, F8 = KV == kKvFp8;
   static constexpr int BS = SH::BS, U = SH::U, CT = U * BS;  // CT tokens per chunk
-  typedef typename std::conditional<I8, f16x8, bf16x8>::type frag_t;
-  typedef typename std::conditional<I8, u32x2, u32x4>::type vword_t;
+  typedef typename std::conditional<BYTE, f16x8, bf16x8>::type frag_t;
+  typedef typename std::conditional<BYTE, u32x2, u32x4>::type vword_t;
   // probabilities handed from the MFMA lanes to the PV lanes: fp32 [token][head] for bf16;
-  // for INT8, fp16 pairs (token t, token t + 8) of p' = p * v_scale, [block][pair][head]
+  // for byte caches, fp16 pairs (token t, token t + 8) of p' = p * v_scale, [block][pair][head]
   struct Lds {
-    float p[I8 ? 1 : CT][GP];
-    uint32_t pp[I8 ? U : 1][8][GP];
+    float p[BYTE ? 1 : CT][GP];
+    uint32_t pp[BYTE ? U : 1][8][GP];
     float alpha[GP];
   };
 
@@ -141,10 +155,10 @@ struct DecodeWave {
     for (int j = 0; j < SH::KSTEPS; ++j) {
       // bf16: step j covers d = 32j + 8*grp + e; INT8: one 16-byte load feeds steps 2jj,
       // 2jj+1 covering d = 64*jj + 16*grp + 8*sub + e.
-      const int d0 = I8 ? (64 * (j / 2) + 16 * grp + 8 * (j % 2)) : (32 * j + 8 * grp);
+      const int d0 = BYTE ? (64 * (j / 2) + 16 * grp + 8 * (j % 2)) : (32 * j + 8 * grp);
       u32x4 w = {0u, 0u, 0u, 0u};
       if (hq < ncol) w = *reinterpret_cast<const u32x4*>(qrow + d0);
-      if constexpr (I8) {
+      if constexpr (BYTE) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           qf[j][2 * e] = (_Float16)bf16_lo(w[e]);
@@ -159,7 +173,7 @@ struct DecodeWave {
       qsum += __shfl_xor(qsum, 16);
       qsum = sum_x32(qsum);
     }
-    bias = kI8Bias * qsum;
+    bias = I8 ? kI8Bias * qsum : 0.f;
   }
 
   __device__ __forceinline__ void reset() {
@@ -191,7 +205,7 @@ struct DecodeWave {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t brow = pool_offset(c.pb[u], Hkv, g, BS, 0, D);
-      if constexpr (I8) {
+      if constexpr (BYTE) {
         const int8_t* kc = reinterpret_cast<const int8_t*>(k_cache) + brow + (int64_t)hq * D;
 #pragma unroll
         for (int jj = 0; jj < SH::KLOADS; ++jj)
@@ -229,14 +243,20 @@ struct DecodeWave {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (I8) {
+      if constexpr (BYTE) {
 #pragma unroll
         for (int jj = 0; jj < SH::KLOADS; ++jj)
 #pragma unroll
           for (int sub = 0; sub < 2; ++sub) {
-            const uint32_t w0 = c.kw[u][jj][2 * sub] ^ 0x80808080u;
-            const uint32_t w1 = c.kw[u][jj][2 * sub + 1] ^ 0x80808080u;
-            const u32x4 hv = {widen_lo(w0), widen_hi(w0), widen_lo(w1), widen_hi(w1)};
+            u32x4 hv;
+            if constexpr (I8) {
+              const uint32_t w0 = c.kw[u][jj][2 * sub] ^ 0x80808080u;
+              const uint32_t w1 = c.kw[u][jj][2 * sub + 1] ^ 0x80808080u;
+              hv = (u32x4){widen_lo(w0), widen_hi(w0), widen_lo(w1), widen_hi(w1)};
+            } else {
+              const uint32_t w0 = c.kw[u][jj][2 * sub], w1 = c.kw[u][jj][2 * sub + 1];
+              hv = (u32x4){fp8x2_lo(w0), fp8x2_hi(w0), fp8x2_lo(w1), fp8x2_hi(w1)};
+            }
             a4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, hv),
                                                         qf[2 * jj + sub], a4, 0, 0, 0);
           }
@@ -252,6 +272,8 @@ struct DecodeWave {
         float s;
         if constexpr (I8)
           s = (a4[i] - bias) * c.ksc[u][i] * scale_log2;
+        else if constexpr (F8)
+          s = a4[i] * (kF8Unscale * c.ksc[u][i]) * scale_log2;
         else
           s = a4[i] * scale_log2;
         sc[u][i] = vis ? s : -INFINITY;
@@ -283,7 +305,7 @@ struct DecodeWave {
       for (int i = 0; i < 4; ++i) {
         const float p = fast_exp2(sc[u][i] - m_run);
         l_part += p;
-        if constexpr (I8) {
+        if constexpr (BYTE) {
           // masked tokens: p = 0 exactly, and their (possibly NaN) scale is not used
           const _Float16 pv16 = (_Float16)(sc[u][i] == -INFINITY ? 0.f : p * c.vsc[u][i]);
           ps_part += (float)pv16;
@@ -295,10 +317,10 @@ struct DecodeWave {
       }
     __builtin_amdgcn_wave_barrier();
     // ---- PV on the VALU -------------------------------------------------------------------
-    if constexpr (I8) {
+    if constexpr (BYTE) {
       // lane (ts, c8) owns tokens ts + TPW*i of each block; it pairs t = ts + TPW*pr with t + 8
-      // and accumulates p'_t (1152 + x_t[d]) with v_dot2_f32_f16 (codes are finite, masked
-      // tokens have p' = 0)
+      // and accumulates p'_t * widened(x_t[d]) with v_dot2_f32_f16 -- INT8: 1152 + x, FP8:
+      // value * 2^-8 (codes are finite, masked tokens have p' = 0)
       constexpr int NPAIR = SH::VLOADS / 2;
       static_assert(SH::TPW * NPAIR == 8, "token pairs are (t, t + 8)");
 #pragma unroll
@@ -307,16 +329,24 @@ struct DecodeWave {
         for (int pr = 0; pr < NPAIR; ++pr) {
           const int pair = ts + SH::TPW * pr;
           const u32x2 bw = c.vw[u][pr], cw = c.vw[u][pr + NPAIR];
-          uint32_t xp[8];  // fp16 pairs (1152 + x_t, 1152 + x_{t+8}) for the lane's 8 d
+          uint32_t xp[8];  // fp16 pairs (token t, token t + 8) for the lane's 8 d
 #pragma unroll
           for (int k = 0; k < 2; ++k) {
-            const uint32_t bx = bw[k] ^ 0x80808080u, cx = cw[k] ^ 0x80808080u;
+            const uint32_t bx = I8 ? bw[k] ^ 0x80808080u : bw[k];
+            const uint32_t cx = I8 ? cw[k] ^ 0x80808080u : cw[k];
             const uint32_t i0 = __builtin_amdgcn_perm(cx, bx, 0x05010400u);  // b0 c0 b1 c1
             const uint32_t i1 = __builtin_amdgcn_perm(cx, bx, 0x07030602u);  // b2 c2 b3 c3
-            xp[4 * k + 0] = widen_lo(i0);
-            xp[4 * k + 1] = widen_hi(i0);
-            xp[4 * k + 2] = widen_lo(i1);
-            xp[4 * k + 3] = widen_hi(i1);
+            if constexpr (I8) {
+              xp[4 * k + 0] = widen_lo(i0);
+              xp[4 * k + 1] = widen_hi(i0);
+              xp[4 * k + 2] = widen_lo(i1);
+              xp[4 * k + 3] = widen_hi(i1);
+            } else {
+              xp[4 * k + 0] = fp8x2_lo(i0);
+              xp[4 * k + 1] = fp8x2_hi(i0);
+              xp[4 * k + 2] = fp8x2_lo(i1);
+              xp[4 * k + 3] = fp8x2_hi(i1);
+            }
           }
           uint32_t pp[GP];
 #pragma unroll
@@ -372,7 +402,7 @@ struct DecodeWave {
 
   // Reduce inside the wave: returns this head's row sum l and sum(p') (lanes hq); afterwards
   // the lanes with ts == 0 hold the complete accumulators of d = 8*c8 .. 8*c8+7, with the
-  // INT8 bias already removed.
+  // INT8 bias already removed (FP8: the 2^-8 of the widened values put back).
   __device__ __forceinline__ void reduce(float& l_w, float& ps_w) {
     l_w = l_part + __shfl_xor(l_part, 16);  // lanes hq, hq+16, hq+32, hq+48
     l_w = sum_x32(l_w);
@@ -395,11 +425,17 @@ struct DecodeWave {
         for (int e = 0; e < 8; ++e) acc[h][e] -= corr;
       }
     }
+    if constexpr (F8) {
+#pragma unroll
+      for (int h = 0; h < GP; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= kF8Unscale;
+    }
   }
 };
 
 // ---- fixed split: one workgroup of 4 waves per (split, g, b) --------------------------------
-template <int D, int GP, bool I8>
+template <int D, int GP, int KV>
 __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, const __half* __restrict__ k_scale,
@@ -408,7 +444,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     float* __restrict__ part_o, float* __restrict__ part_lse, int Hq, int Hkv, int G, int QL,
     int max_blocks, int num_blocks, int max_ctx, float scale_log2, int window, int C,
     int n_split) {
-  using W = DecodeWave<D, GP, I8>;
+  using W = DecodeWave<D, GP, KV>;
   constexpr int BS = W::BS, U = W::U;
   __shared__ typename W::Lds s_lds[kDecodeWaves];
   __shared__ float s_red[kDecodeWaves][GP][D];
@@ -582,7 +618,7 @@ __device__ __forceinline__ int visible_blocks(const int32_t* __restrict__ ctx_le
   return (ctx + 15) / 16 - first_key(ctx, QL, window) / 16;
 }
 
-template <int D, int GP, bool I8>
+template <int D, int GP, int KV>
 __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, const __half* __restrict__ k_scale,
@@ -591,7 +627,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
     int32_t* __restrict__ prefix_out, float* __restrict__ part_o, float* __restrict__ part_lse,
     int B, int Hq, int Hkv, int G, int QL, int max_blocks, int num_blocks, int max_ctx,
     float scale_log2, int window) {
-  using W = DecodeWave<D, GP, I8>;
+  using W = DecodeWave<D, GP, KV>;
   constexpr int BS = W::BS, U = W::U;
   __shared__ typename W::Lds s_lds[kDecodeWaves];
   __shared__ int s_pre[kStreamMaxB + 1];
@@ -812,9 +848,9 @@ DecodePlan plan_decode(int B, int QL, int Hq, int Hkv, int D, int max_context_le
   return p;
 }
 
-template <int D, int GP, bool I8>
+template <int D, int GP, int KV>
 static void launch_stream(const DecodeArgs& a, hipStream_t stream) {
-  const auto kern = decode_stream_kernel<D, GP, I8>;
+  const auto kern = decode_stream_kernel<D, GP, KV>;
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kDecodeThreads, 0) != hipSuccess ||
       per_cu < 1)
@@ -835,14 +871,14 @@ static void launch_stream(const DecodeArgs& a, hipStream_t stream) {
                      a.q_len, wgs * kDecodeWaves);
 }
 
-template <int D, int GP, bool I8>
+template <int D, int GP, int KV>
 static void launch_split(const DecodeArgs& a, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
   const int C = a.plan.split_tokens, ns = a.plan.n_split;
   char* ws = reinterpret_cast<char*>(a.workspace);
   float* part_o = ns > 1 ? reinterpret_cast<float*>(ws + a.plan.part_o_off) : nullptr;
   float* part_lse = ns > 1 ? reinterpret_cast<float*>(ws + a.plan.part_lse_off) : nullptr;
-  hipLaunchKernelGGL((decode_split_kernel<D, GP, I8>), dim3(a.Hkv, a.B, ns), dim3(kDecodeThreads),
+  hipLaunchKernelGGL((decode_split_kernel<D, GP, KV>), dim3(a.Hkv, a.B, ns), dim3(kDecodeThreads),
                      0, stream, (const uint16_t*)a.q, a.k_cache, a.v_cache,
                      (const __half*)a.k_scale, (const __half*)a.v_scale, a.block_table,
                      a.context_lens, (uint16_t*)a.o, part_o, part_lse, a.Hq, a.Hkv, G, a.q_len,
@@ -854,31 +890,39 @@ static void launch_split(const DecodeArgs& a, hipStream_t stream) {
                        a.max_blocks_per_seq, a.max_context_len, a.window, C, ns);
 }
 
-template <int D, int GP, bool I8>
+template <int D, int GP, int KV>
 static void launch_shape(const DecodeArgs& a, hipStream_t stream) {
   if (a.plan.stream)
-    launch_stream<D, GP, I8>(a, stream);
+    launch_stream<D, GP, KV>(a, stream);
   else
-    launch_split<D, GP, I8>(a, stream);
+    launch_split<D, GP, KV>(a, stream);
 }
 
-template <int D, bool I8>
+template <int D, int KV>
 static void launch_g(const DecodeArgs& a, hipStream_t stream) {
   switch (pow2_at_least(a.Hq / a.Hkv * a.q_len)) {  // MFMA columns: (query row, head) pairs
-    case 1: launch_shape<D, 1, I8>(a, stream); break;
-    case 2: launch_shape<D, 2, I8>(a, stream); break;
-    case 4: launch_shape<D, 4, I8>(a, stream); break;
-    case 8: launch_shape<D, 8, I8>(a, stream); break;
-    default: launch_shape<D, 16, I8>(a, stream); break;
+    case 1: launch_shape<D, 1, KV>(a, stream); break;
+    case 2: launch_shape<D, 2, KV>(a, stream); break;
+    case 4: launch_shape<D, 4, KV>(a, stream); break;
+    case 8: launch_shape<D, 8, KV>(a, stream); break;
+    default: launch_shape<D, 16, KV>(a, stream); break;
+  }
+}
+
+template <int D>
+static void launch_kv(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.kv) {
+    case kKvI8: launch_g<D, kKvI8>(a, stream); break;
+    case kKvFp8: launch_g<D, kKvFp8>(a, stream); break;
+    default: launch_g<D, kKvBf16>(a, stream); break;
   }
 }
 
 int launch_decode(const DecodeArgs& a, hipStream_t stream) {
-  if (a.D == 64) {
-    if (a.int8) launch_g<64, true>(a, stream); else launch_g<64, false>(a, stream);
-  } else {
-    if (a.int8) launch_g<128, true>(a, stream); else launch_g<128, false>(a, stream);
-  }
+  if (a.D == 64)
+    launch_kv<64>(a, stream);
+  else
+    launch_kv<128>(a, stream);
   return 0;
 }
 

@@ -18,6 +18,10 @@ struct PrefillArgs {
   int causal, window;
 };
 
+// KV-cache element kinds (bf16 values, INT8 codes, FP8 E4M3 codes; byte kinds carry fp16
+// per-(token, KV head) scales)
+constexpr int kKvBf16 = 0, kKvI8 = 1, kKvFp8 = 2;
+
 constexpr int kMaxSplitTokens = 8192;  // largest split_tokens a decode call accepts
 constexpr int kStreamMaxB = 2048;      // largest batch of the balanced decode shape
 
@@ -39,7 +43,7 @@ struct DecodeArgs {
   const int32_t* block_table;
   const int32_t* context_lens;
   void* o;
-  bool int8;
+  int kv;  // cache element kind: kKvBf16, kKvI8 or kKvFp8
   int B, q_len, Hq, Hkv, D, block_size, max_blocks_per_seq, num_blocks, max_context_len;
   float scale;
   int window;
@@ -57,7 +61,7 @@ struct AppendArgs {
   void* v_cache;
   void* k_scale;
   void* v_scale;
-  bool int8;
+  int kv;  // cache element kind: kKvBf16, kKvI8 or kKvFp8
   int T, Hkv, D, block_size, num_seqs, max_blocks_per_seq, num_blocks;
 };
 

@@ -427,7 +427,7 @@ int launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
 int launch_prefill_paged(const PrefillPagedArgs& a, hipStream_t stream) {
   if (a.k_new != nullptr) {
     AppendArgs ap{a.k_new, a.v_new, nullptr, nullptr, a.table, a.k_cache, a.v_cache, nullptr,
-                  nullptr, false, a.total_q, a.Hkv, a.D, 16, a.B, a.max_blocks_per_seq,
+                  nullptr, kKvBf16, a.total_q, a.Hkv, a.D, 16, a.B, a.max_blocks_per_seq,
                   a.num_blocks};
     launch_kv_append_varlen(ap, a.cu_q, a.ctx, stream);
   }

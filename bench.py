@@ -14,7 +14,9 @@ is reported beside it. `--workload swa` / `int8_70b` time the other configuratio
 Outside the timed steps, the default run also times attn_prefill_paged (chunked prefill over
 the paged cache with fused append: 4 sequences, 1024-token chunks after 3072-token prefixes)
 attn_decode_paged_multi (4 draft rows per sequence on the decode cache) and
-kv_cache_append_rope (a 64k-token prompt written into a paged cache with RoPE on K).
+kv_cache_append_rope (a 64k-token prompt written into a paged cache with RoPE on K) and
+attn_decode_paged over an FP8 E4M3 copy of the decode cache. `--workload fp8_70b` runs the
+INT8 70B-shaped decode with an FP8 cache instead.
 
 Prints one JSON line. Inputs are seeded synthetic tensors (synth/) resident in HBM before the
 timed region starts.
@@ -84,8 +86,8 @@ def prefill_flops(wl) -> float:
 
 def decode_bytes(wl, ctx) -> float:
     vis = np.minimum(ctx, wl.window) if wl.window > 0 else ctx
-    per_tok = 2 * wl.Hkv * wl.D * (1 if wl.kv_dtype == "i8" else 2)
-    if wl.kv_dtype == "i8":
+    per_tok = 2 * wl.Hkv * wl.D * (1 if wl.kv_dtype in ("i8", "fp8") else 2)
+    if wl.kv_dtype in ("i8", "fp8"):
         per_tok += 2 * wl.Hkv * 2  # fp16 scales of K and V
     return float(vis.sum()) * per_tok + 2.0 * wl.B * wl.Hq * wl.D * 2
 
@@ -124,7 +126,8 @@ def setup_decode(t, wl):
             src = pool(wl, which, nb)
             rows = _bf16(t, np.ascontiguousarray(src.transpose(0, 2, 1, 3)).reshape(T, wl.Hkv, wl.D))
             del src
-            c = t.empty((nb, wl.Hkv, wl.block_size, wl.D), dtype=t.int8, device="cuda")
+            c = t.empty((nb, wl.Hkv, wl.block_size, wl.D), dtype=t.int8 if wl.kv_dtype == "i8" else t.uint8,
+                        device="cuda")
             s = t.empty((nb, wl.Hkv, wl.block_size), dtype=t.float16, device="cuda")
             A.kv_cache_append(rows, rows, seq, pos, ident, c, c, k_scale=s, v_scale=s)
             t.cuda.synchronize()
@@ -266,6 +269,49 @@ def time_append_rope(t, A, reps: int):
             "workload": f"{T} tokens ({B} x {S}), Hkv={Hkv} D={D} bf16, RoPE base 500000, permuted pool"}
 
 
+def time_decode_fp8(t, A, dwl, Dd, reps: int):
+    """attn_decode_paged over an FP8 E4M3 copy of the decode workload's bf16 cache (quantized
+    on the GPU by kv_cache_append), timed per call after a cache-evicting read."""
+    import dataclasses
+    nb = Dd["nb"]
+    T = nb * dwl.block_size
+    ident = t.arange(nb, dtype=t.int32, device="cuda")[None]
+    seq = t.zeros(T, dtype=t.int32, device="cuda")
+    pos = t.arange(T, dtype=t.int32, device="cuda")
+    q8 = {}
+    for which in ("k", "v"):
+        rows = Dd[which + "c"].permute(0, 2, 1, 3).contiguous().view(T, dwl.Hkv, dwl.D)
+        c = t.empty((nb, dwl.Hkv, dwl.block_size, dwl.D), dtype=t.uint8, device="cuda")
+        s = t.empty((nb, dwl.Hkv, dwl.block_size), dtype=t.float16, device="cuda")
+        A.kv_cache_append(rows, rows, seq, pos, ident, c, c, k_scale=s, v_scale=s)
+        del rows
+        q8[which] = (c, s)
+    flush = t.ones(512 * 1024 * 1024 // 4, dtype=t.float32, device="cuda")
+    o = t.empty_like(Dd["q"])
+
+    def call():
+        A.attn_decode_paged(Dd["q"], q8["k"][0], q8["v"][0], Dd["table"], Dd["ctx"], dwl.ctx_hi,
+                            k_scale=q8["k"][1], v_scale=q8["v"][1], scale=dwl.scale, window=dwl.window,
+                            out=o)
+    call()
+    ms = []
+    for _ in range(reps):
+        flush.sum()
+        e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        t.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    ms = float(np.mean(ms))
+    byts = decode_bytes(dataclasses.replace(dwl, kv_dtype="fp8"), Dd["ctx_np"])
+    gbs = byts / (ms * 1e-3) / 1e9
+    return {"kernel": "attn_decode_paged (FP8 E4M3 cache)", "ms": ms, "GB/s": gbs,
+            "frac_hbm_peak": gbs / HBM_PEAK_GBS, "algorithmic_bytes": byts, "calls": reps,
+            "tokens_per_s": dwl.B / (ms * 1e-3),
+            "workload": f"{dwl.name} shapes with the cache quantized to FP8 E4M3 + fp16 per-token scales"}
+
+
 def cpu_baseline(pwl, dwl, budget_s: float):
     """The oracle, untuned, on a time-bounded sample of the same workload."""
     import oracle
@@ -297,7 +343,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama1b", choices=["llama1b", "swa", "int8_70b"])
+    ap.add_argument("--workload", default="llama1b", choices=["llama1b", "swa", "int8_70b", "fp8_70b"])
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0 = skip)")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache-evicting scratch read")
     ap.add_argument("--no-chunked", action="store_true",
@@ -324,10 +370,13 @@ def main(argv=None):
         print(json.dumps({"copy_calibration_bytes": COPY_CALIBRATION_BYTES, "launches": 3}))
         return 0
 
+    import dataclasses
     pwl = {"llama1b": WORKLOADS["prefill_llama1b_s4096"], "swa": WORKLOADS["prefill_swa_s16384"],
-           "int8_70b": None}[args.workload]
+           "int8_70b": None, "fp8_70b": None}[args.workload]
+    c5 = WORKLOADS["decode_int8_70b_b16"]
     dwl = {"llama1b": WORKLOADS["decode_llama1b_b64"], "swa": WORKLOADS["decode_swa_b32"],
-           "int8_70b": WORKLOADS["decode_int8_70b_b16"]}[args.workload]
+           "int8_70b": c5,
+           "fp8_70b": dataclasses.replace(c5, name="decode_fp8_70b_b16", kv_dtype="fp8")}[args.workload]
 
     P = setup_prefill(t, pwl) if pwl else None
     Dd = setup_decode(t, dwl)
@@ -408,6 +457,7 @@ def main(argv=None):
         out["prefill_paged"] = time_chunked(t, A, max(5, args.steps))
         out["decode_multi"] = time_decode_multi(t, A, dwl, Dd, max(5, args.steps))
         out["append_rope"] = time_append_rope(t, A, max(5, args.steps))
+        out["decode_fp8"] = time_decode_fp8(t, A, dwl, Dd, max(5, args.steps))
     if args.cpu_budget > 0 and pwl is not None:
         out["cpu_baseline"] = cpu_baseline(pwl, dwl, args.cpu_budget)
     print(json.dumps(out), flush=True)

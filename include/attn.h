@@ -57,7 +57,10 @@ enum attn_status {
   ATTN_ERR_HIP = 6          /* a HIP launch failed; attn_last_error() holds the HIP message */
 };
 
-enum attn_dtype { ATTN_F32 = 0, ATTN_BF16 = 1, ATTN_I8 = 2 };
+/* ATTN_I8 and ATTN_FP8 are KV-cache element types only (codes with fp16 scales); ATTN_FP8 is
+ * OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, largest finite 448,
+ * S.1111.111 = NaN, no infinities), stored one code per byte. */
+enum attn_dtype { ATTN_F32 = 0, ATTN_BF16 = 1, ATTN_I8 = 2, ATTN_FP8 = 3 };
 
 /*
  * attn_prefill -- tiled (FlashAttention-style) prefill attention with an online softmax.
@@ -121,12 +124,14 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_context
  *
  *  q, o         : [B][Hq][D] bf16. Query b sits at position context_lens[b] - 1.
  *  k_cache,
- *  v_cache      : [num_blocks][Hkv][block_size][D], bf16 (kv_dtype ATTN_BF16) or int8
- *                 (ATTN_I8). Logical token t of sequence b lives in slot t % block_size of
+ *  v_cache      : [num_blocks][Hkv][block_size][D], bf16 (kv_dtype ATTN_BF16), int8 codes
+ *                 (ATTN_I8) or FP8 E4M3 codes (ATTN_FP8; [TF] "3.3 FP8量化支持").
+ *                 Logical token t of sequence b lives in slot t % block_size of
  *                 physical block block_table[b][t / block_size].
  *  k_scale,
- *  v_scale      : fp16 [num_blocks][Hkv][block_size], required iff kv_dtype == ATTN_I8, else
- *                 NULL. The value seen by attention is code * scale.
+ *  v_scale      : fp16 [num_blocks][Hkv][block_size], required iff kv_dtype is ATTN_I8 or
+ *                 ATTN_FP8, else NULL. The value seen by attention is value(code) * scale
+ *                 (INT8: the integer; FP8: the E4M3 value). FP8 NaN codes must not be stored.
  *  block_table  : int32 [B][max_blocks_per_seq]. Entries for blocks that hold no visible
  *                 token (past the context, or wholly left of the window) are never read and
  *                 may hold anything. A live entry outside [0, num_blocks) is not dereferenced:
@@ -203,7 +208,10 @@ int attn_decode_paged_multi(const void* q, const void* k_cache, const void* v_ca
  *                 the bits; ATTN_I8 quantizes each (token, KV head) row of D values:
  *                 a = max|x|, scale = fp16(fp32(a) / 127) (IEEE division, round to nearest
  *                 even), code = clamp(rint(x / fp32(scale)), -127, 127) with ties to even; a
- *                 zero scale gives zero codes.
+ *                 zero scale gives zero codes. ATTN_FP8 ([TF] "3.3 FP8量化支持", dynamic
+ *                 per-token scale): scale = fp16(fp32(a) / 448), code = the E4M3 value nearest
+ *                 to clamp(x / fp32(scale), -448, 448), ties to even, sign kept (-0 -> 0x80);
+ *                 a zero scale gives zero codes.
  *  Rows whose seq_idx is outside [0, num_seqs), whose pos is outside
  *  [0, max_blocks_per_seq*block_size), or whose table entry is outside [0, num_blocks) are not
  *  written. Two rows aimed at the same slot leave one of them, unspecified which.

@@ -16,7 +16,8 @@ What the pages fix, and where (page title, section):
        - 推测性解码与INT8量化: the KV cache is stored as INT8 instead of FP16.
   [IL] "从零开始的LLM推理优化实验室：从PyTorch基线到Triton内核的完整实践", KV缓存实验与长上下文优化:
        static, growing and sliding-window KV caches.
-  [TF] "Triton融合算子优化：LLM推理性能提升3倍的工程实践", 3.1 RMSNorm + RoPE 融合: rotary
+  [TF] "Triton融合算子优化：LLM推理性能提升3倍的工程实践", 3.3 FP8量化支持: FP8 E4M3 with a
+       dynamic per-token scale; 3.1 RMSNorm + RoPE 融合: rotary
        position embedding applied to rows at their position ids, fused with the neighbouring
        elementwise step so the rows cross HBM once; [TI] 技术架构与模块设计 lists RoPE among the
        Llama 3.2 1B operators.
@@ -33,6 +34,11 @@ Readings where the pages are silent (the same list is kept in the design notes):
     nearest-even), code = clamp(rint(fp32(x) / fp32(s)), -127, 127) with rint ties-to-even;
     s == 0 (a == 0, or a / 127 below half the smallest fp16 subnormal) gives code 0; the
     dequantized value the attention sees is code * s, exactly;
+  * FP8 KV: E4M3 as defined by the OCP 8-bit floating point format (1 sign, 4 exponent bits with
+    bias 7, 3 mantissa bits, subnormals, largest finite 448, S.1111.111 = NaN, no infinities);
+    per token and KV head a = max|x|, s = fp16(fp32(a) / 448), code = E4M3 of
+    clamp(fp32(x) / fp32(s), -448, 448) rounded to nearest-even, sign kept (so -0 is 0x80);
+    s == 0 gives code 0; the value attention sees is decode(code) * s;
   * RoPE (the pages name it, give no formula): the Llama convention -- dimension i < D/2 is
     paired with i + D/2 and the pair is rotated by the angle pos * base^(-2i/D); the rotated
     fp64 value is rounded to fp32 and then to bf16 (both to nearest-even) when stored as bf16.
@@ -47,6 +53,7 @@ __all__ = [
     "visible_mask", "attention_head", "attention", "gather_logical", "decode_paged", "rope",
     "bf16_round",
     "prefill_paged", "quantize_int8", "dequantize_int8", "append_expected", "merge_partials",
+    "fp8_e4m3_decode", "fp8_e4m3_encode", "quantize_fp8", "dequantize_fp8",
 ]
 
 
@@ -210,6 +217,54 @@ def quantize_int8(x):
     q = np.clip(q, -127, 127)
     q = np.where((s32 == 0)[..., None], 0, q)
     return q.astype(np.int8), s16
+
+
+def fp8_e4m3_decode(codes):
+    """Value of E4M3 codes (uint8) in float64: sign * 2^(e-7) * (1 + m/8), or for e == 0 the
+    subnormal sign * 2^-6 * m/8; code 0x7f / 0xff is NaN."""
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e, m = (c >> 3) & 0xF, c & 0x7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    return np.where((c & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+def fp8_e4m3_encode(x):
+    """Nearest E4M3 code (ties to the even code) of float values |x| <= 448, by comparing with
+    the decoded values of all 127 non-negative finite codes; the sign bit is x's (so negative
+    values that round to zero give 0x80, -0)."""
+    x = np.asarray(x, np.float64)
+    if np.any(np.abs(x) > 448) or np.any(np.isnan(x)):
+        raise ValueError("fp8_e4m3_encode expects |x| <= 448")
+    grid = fp8_e4m3_decode(np.arange(127, dtype=np.uint8))  # 0 .. 448, increasing
+    a = np.abs(x)
+    hi = np.clip(np.searchsorted(grid, a, side="left"), 0, 126)  # first grid value >= a
+    lo = np.clip(hi - 1, 0, 126)
+    d_lo, d_hi = a - grid[lo], grid[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a == grid[hi], hi, code)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)  # -0 keeps its sign
+
+
+def quantize_fp8(x):
+    """Per-row FP8 E4M3 quantization of the last axis, in fp32 as the kernel does it.
+
+    x: float32 [...][D]. Returns (codes uint8 [...][D], scales float16 [...]).
+    """
+    x = np.asarray(x, np.float32)
+    a = np.abs(x).max(axis=-1)
+    s16 = (a / np.float32(448.0)).astype(np.float16)
+    s32 = s16.astype(np.float32)
+    safe = np.where(s32 == 0, np.float32(1.0), s32)
+    y = np.clip(x / safe[..., None], np.float32(-448.0), np.float32(448.0))
+    codes = fp8_e4m3_encode(y.astype(np.float64))
+    return np.where((s32 == 0)[..., None], 0, codes).astype(np.uint8), s16
+
+
+def dequantize_fp8(codes, scales):
+    """Exact value decode(code) * scale in float64; codes [...][D] uint8, scales [...] fp16."""
+    return fp8_e4m3_decode(codes) * np.asarray(scales, np.float64)[..., None]
 
 
 def append_expected(pool, rows, seq_idx, pos, table, block_size: int):

@@ -27,11 +27,11 @@ __all__ = [
     "PrefillWorkload", "DecodeWorkload", "WORKLOADS",
     "bf16_bits", "bf16_value", "prefill_slab", "prefill_inputs", "decode_query",
     "context_lens", "paged_table", "pool_blocks", "pool", "int8_pool_blocks", "int8_pool",
-    "new_tokens",
+    "fp8_pool", "new_tokens",
 ]
 
 # tensor ids for seeding sub-streams
-_Q, _K, _V, _CTX, _PERM, _KNEW, _VNEW, _KI8, _VI8 = range(1, 10)
+_Q, _K, _V, _CTX, _PERM, _KNEW, _VNEW, _KI8, _VI8, _KF8, _VF8 = range(1, 12)
 _POOL_CHUNK = 64
 
 
@@ -215,6 +215,21 @@ def int8_pool_blocks(wl: DecodeWorkload, which: str, blocks):
 
 def int8_pool(wl: DecodeWorkload, which: str, num_blocks: int):
     return int8_pool_blocks(wl, which, np.arange(num_blocks))
+
+
+def fp8_pool(wl: DecodeWorkload, which: str, num_blocks: int):
+    """Directly drawn FP8 E4M3 codes [n][Hkv][bs][D] and fp16 scales [n][Hkv][bs] (uniform in
+    [0.5, 1.5) / 64), for decode tests that bypass quantization. Codes are uniform over the
+    bytes 0x00-0x67 and 0x80-0xE7 (exponent field at most 12: magnitudes up to 60, so values
+    times scales stay within about +-1.4, the range of N(0,1) data). Byte values only: no
+    format arithmetic happens here."""
+    tid = {"k": _KF8, "v": _VF8}[which]
+    r = _rng(wl.seed, tid, 0)
+    b = r.integers(0, 2 * 0x68, size=(num_blocks, wl.Hkv, wl.block_size, wl.D), dtype=np.int64)
+    codes = np.where(b >= 0x68, b - 0x68 + 0x80, b).astype(np.uint8)
+    scales = ((0.5 + r.random((num_blocks, wl.Hkv, wl.block_size), dtype=np.float32))
+              * np.float32(1.0 / 64.0)).astype(np.float16)
+    return codes, scales
 
 
 def new_tokens(seed: int, T: int, Hkv: int, D: int, which: str) -> tuple[np.ndarray, np.ndarray]:

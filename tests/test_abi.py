@@ -193,3 +193,11 @@ def test_rope_inplace_validation(kw, code):
     a = dict(x=FAKE, T=3, H=2, D=64, base=10000.0)
     a.update(kw)
     assert A.lib().attn_rope_inplace(a["x"], FAKE, a["T"], a["H"], a["D"], a["base"], None) == code
+
+
+def test_fp8_cache_validation():
+    assert _decode(kv=A.ATTN_FP8) == A.ATTN_ERR_NULL            # fp8 cache without scales
+    assert _decode(kv=A.ATTN_FP8, ks=FAKE) == A.ATTN_ERR_NULL
+    assert _decode(kv=4) == A.ATTN_ERR_DTYPE
+    assert _append(dt=A.ATTN_FP8) == A.ATTN_ERR_NULL
+    assert _append(dt=A.ATTN_FP8, T=0, kn=None) == A.ATTN_OK

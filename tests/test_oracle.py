@@ -528,3 +528,41 @@ def test_bf16_round_hand_values():
     # the rounding agrees with the bit-level generator's on random fp32 values
     x = np.random.default_rng(2).standard_normal(1000).astype(np.float32)
     assert np.array_equal(oracle.bf16_round(x), bf16_value(bf16_bits(x)))
+
+
+# ---- FP8 E4M3 (OCP format: bias 7, 3 mantissa bits, max 448, S.1111.111 NaN) --------------
+def test_fp8_decode_hand_values():
+    vals = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0, 0x39: 1.125,
+            0x3F: 1.875, 0x40: 2.0, 0x7E: 448.0, 0x80: -0.0, 0xB8: -1.0, 0xFE: -448.0, 0x30: 0.5}
+    for code, v in vals.items():
+        assert oracle.fp8_e4m3_decode(np.uint8(code)) == v, hex(code)
+    assert np.isnan(oracle.fp8_e4m3_decode(np.uint8(0x7F))) and np.isnan(oracle.fp8_e4m3_decode(np.uint8(0xFF)))
+
+
+def test_fp8_encode_round_trip_and_ties():
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    assert np.array_equal(oracle.fp8_e4m3_encode(oracle.fp8_e4m3_decode(codes)), codes)
+    # ties go to the even code; just above / below a tie go to the nearer code
+    assert oracle.fp8_e4m3_encode(1.0625) == 0x38      # between 1 (even) and 1.125
+    assert oracle.fp8_e4m3_encode(1.1875) == 0x3A      # between 1.125 and 1.25 (even)
+    assert oracle.fp8_e4m3_encode(1.0625 + 1e-9) == 0x39
+    assert oracle.fp8_e4m3_encode(2.0 ** -10) == 0x00  # half the smallest subnormal: to 0 (even)
+    assert oracle.fp8_e4m3_encode(1.5 * 2.0 ** -9) == 0x02
+    assert oracle.fp8_e4m3_encode(-3.0) == 0xC4 and oracle.fp8_e4m3_encode(440.0) == 0x7E
+    assert oracle.fp8_e4m3_encode(-2.0 ** -11) == 0x80  # rounds to -0
+    with pytest.raises(ValueError):
+        oracle.fp8_e4m3_encode(449.0)
+
+
+def test_fp8_quantizer_bounds():
+    x = np.random.default_rng(3).standard_normal((50, 128)).astype(np.float32)
+    codes, s = oracle.quantize_fp8(x)
+    y = oracle.dequantize_fp8(codes, s)
+    s64 = s.astype(np.float64)[:, None]
+    # relative error of E4M3 is at most 2^-4 of the value, or half a subnormal step (2^-10 s)
+    assert (np.abs(y - x) <= np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * s64) * 1.0001).all()
+    # the absmax element maps to (nearly) +-448: its code is 0x7E / 0xFE or one step below
+    amax = np.abs(oracle.fp8_e4m3_decode(codes)).max(axis=1)
+    assert (amax >= 416).all() and (amax <= 448).all()
+    z, sz = oracle.quantize_fp8(np.zeros((2, 64), np.float32))
+    assert (z == 0).all() and (sz == 0).all()
