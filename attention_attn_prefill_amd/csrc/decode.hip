@@ -68,17 +68,14 @@ __device__ __forceinline__ uint32_t widen_lo(uint32_t u) { return __builtin_amdg
 __device__ __forceinline__ uint32_t widen_hi(uint32_t u) { return __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u); }
 constexpr float kI8Bias = 1152.0f;
 
-// FP8 E4M3 -> fp16 without conversions: for a code c, the fp16 bit pattern
-// ((c & 0x7f) << 7) | ((c & 0x80) << 8) is exactly value(c) * 2^-8 (the 4-bit exponent with bias
-// 7 lands in fp16's 5-bit exponent with bias 15, subnormals included; NaN codes are never
-// stored). fp8x2_lo / fp8x2_hi turn bytes 0, 1 / 2, 3 of u into an fp16 pair; the 2^8 is put
-// back on the scores and the accumulators.
-__device__ __forceinline__ uint32_t fp8x2(uint32_t v) {  // v: bytes at bits 0-7 and 16-23
-  return ((v & 0x007f007fu) << 7) | ((v & 0x00800080u) << 8);
+// FP8 E4M3 -> fp16 pair with gfx950's packed conversion (scale 1): every E4M3 value,
+// subnormals included, is exact in fp16. fp8x2_lo / fp8x2_hi convert bytes 0, 1 / 2, 3 of u.
+__device__ __forceinline__ uint32_t fp8x2_lo(uint32_t u) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(u, 1.0f, false));
 }
-__device__ __forceinline__ uint32_t fp8x2_lo(uint32_t u) { return fp8x2(__builtin_amdgcn_perm(0u, u, 0x0c010c00u)); }
-__device__ __forceinline__ uint32_t fp8x2_hi(uint32_t u) { return fp8x2(__builtin_amdgcn_perm(0u, u, 0x0c030c02u)); }
-constexpr float kF8Unscale = 256.0f;
+__device__ __forceinline__ uint32_t fp8x2_hi(uint32_t u) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(u, 1.0f, true));
+}
 
 // xor-16 / xor-32 lane partners within a wave
 __device__ __forceinline__ float max_x32(float x) {
@@ -273,7 +270,7 @@ struct DecodeWave {
         if constexpr (I8)
           s = (a4[i] - bias) * c.ksc[u][i] * scale_log2;
         else if constexpr (F8)
-          s = a4[i] * (kF8Unscale * c.ksc[u][i]) * scale_log2;
+          s = a4[i] * c.ksc[u][i] * scale_log2;
         else
           s = a4[i] * scale_log2;
         sc[u][i] = vis ? s : -INFINITY;
@@ -320,7 +317,7 @@ struct DecodeWave {
     if constexpr (BYTE) {
       // lane (ts, c8) owns tokens ts + TPW*i of each block; it pairs t = ts + TPW*pr with t + 8
       // and accumulates p'_t * widened(x_t[d]) with v_dot2_f32_f16 -- INT8: 1152 + x, FP8:
-      // value * 2^-8 (codes are finite, masked tokens have p' = 0)
+      // the E4M3 value (codes are finite, masked tokens have p' = 0)
       constexpr int NPAIR = SH::VLOADS / 2;
       static_assert(SH::TPW * NPAIR == 8, "token pairs are (t, t + 8)");
 #pragma unroll
@@ -402,7 +399,7 @@ struct DecodeWave {
 
   // Reduce inside the wave: returns this head's row sum l and sum(p') (lanes hq); afterwards
   // the lanes with ts == 0 hold the complete accumulators of d = 8*c8 .. 8*c8+7, with the
-  // INT8 bias already removed (FP8: the 2^-8 of the widened values put back).
+  // INT8 bias already removed.
   __device__ __forceinline__ void reduce(float& l_w, float& ps_w) {
     l_w = l_part + __shfl_xor(l_part, 16);  // lanes hq, hq+16, hq+32, hq+48
     l_w = sum_x32(l_w);
@@ -425,12 +422,7 @@ struct DecodeWave {
         for (int e = 0; e < 8; ++e) acc[h][e] -= corr;
       }
     }
-    if constexpr (F8) {
-#pragma unroll
-      for (int h = 0; h < GP; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] *= kF8Unscale;
-    }
+
   }
 };
 
