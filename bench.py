@@ -39,9 +39,9 @@ import numpy as np  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 COPY_CALIBRATION_BYTES = 256 * 1024 * 1024  # each direction of the calibration copy
-KERNEL_SOURCES = {
-    "prefill_bf16_kernel": "attention_attn_prefill_amd/csrc/prefill_bf16.hip",
-    "decode_split_kernel": "attention_attn_prefill_amd/csrc/decode.hip",
+KERNEL_SOURCES = {  # the source each measured call's kernels come from
+    "prefill": "attention_attn_prefill_amd/csrc/prefill_bf16.hip",
+    "decode": "attention_attn_prefill_amd/csrc/decode.hip",
 }
 
 
@@ -52,7 +52,7 @@ def source_hash(kernel: str) -> str:
 
 
 def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or
+    """HBM bytes per call from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or
     None when there is none or the kernel source changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
     if not os.path.exists(path):
@@ -429,7 +429,7 @@ def main(argv=None):
                           f"ctx=[{dwl.ctx_lo},{dwl.ctx_hi}] window={dwl.window} block=16"}
     roofline_decode = {"bound": "hbm", "achieved": d_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": d_gbs / HBM_PEAK_GBS,
-                       "traffic": measured_traffic("decode_split_kernel", dwl.name)}
+                       "traffic": measured_traffic("decode", dwl.name)}
     out = {"metric": "paged decode attn HBM GB/s (% peak); prefill attn TFLOP/s (% MFMA peak)",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
@@ -441,7 +441,7 @@ def main(argv=None):
         out.update(value=p_tf, unit="TFLOP/s")
         out["roofline"] = {"bound": "mfma", "achieved": p_tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": p_tf / BF16_PEAK_TFLOPS,
-                           "traffic": measured_traffic("prefill_bf16_kernel", pwl.name)}
+                           "traffic": measured_traffic("prefill", pwl.name)}
         out["prefill"] = {"kernel": "attn_prefill (bf16 MFMA)", "ms": p_ms, "TFLOP/s": p_tf,
                           "algorithmic_flops": pfl, "tokens_per_s": pwl.B * pwl.S / (p_ms * 1e-3),
                           "workload": f"{pwl.name}: B={pwl.B} S={pwl.S} Hq={pwl.Hq} Hkv={pwl.Hkv} "
