@@ -26,8 +26,10 @@
 //    O^T += V^T P^T. The V^T operand is read from the natural V tile with ds_read_b64_tr_b16
 //    (each lane receives 4 consecutive keys of one d), addressed so that its keys line up with
 //    the keys the score accumulator put in the same lane.
-//  * Tiles entirely hidden by the causal mask or the window are never visited; the mask is
-//    applied only on tiles that straddle an edge. exp2 with scale*log2(e) folded into one FMA;
+//  * Tiles hidden by the causal mask or the window from every row of the workgroup are never
+//    visited; the mask is applied only on tiles that straddle an edge of the wave's rows (or lie
+//    outside them, when another wave of the workgroup needs the tile). exp2 with
+//    scale*log2(e) folded into one FMA;
 //    the running max moves only when it grows by more than kRescaleSlack.
 #include "common.h"
 #include "launch.h"
@@ -181,8 +183,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(
   f32x16 oacc[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
+    oacc[i] = (f32x16){};
   float m_run = kNegBig, l_run = 0.f;
 
   // ---- direct global -> LDS tile loads ---------------------------------------------------
@@ -269,10 +270,12 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(
     }
   }
 
-  // One tile step for this wave. MASK selects the edge-tile variant (causal diagonal, window
-  // edge or the ragged end of the sequence); interior tiles skip all mask arithmetic.
-  auto tile_step = [&](const char* st_base, int k0, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+  // One tile step for this wave. `masked` (wave-uniform) applies the causal, window and
+  // ragged-end masks; interior tiles skip that arithmetic. There is a single copy of the step
+  // in the loop: separate masked/unmasked copies, or skipping the step on some paths, make
+  // the compiler merge the O accumulators from several paths into registers that are not the
+  // MFMA's tuples, and it then copies all of them every tile.
+  auto tile_step = [&](const char* st_base, int k0, bool masked) {
     // S^T = K Q^T; the two 32-key blocks alternate so consecutive MFMAs are independent
     // (a dependent accumulation chain would wait for each result)
     f32x16 sacc[kBN / 32];
@@ -287,7 +290,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(st_base + kaddr_t[t] + kb * 32 * T::ROWB);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], sacc[kb], 0, 0, 0);
       }
-    if constexpr (MASK) {
+    if (masked) {
       // register r of block kb holds key offset 32*kb + 8*(r/4) + (r%4) + 4*half of the tile
       const int qp = off + q0w + col;  // query position
       int hi = Lk - 1 - k0;
@@ -315,8 +318,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(
       m_run = m_new;
 #pragma unroll
       for (int i = 0; i < DB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+        oacc[i] *= alpha;
     }
     float rs = 0.f;
     bf16x8 pf[kBN / 16];
@@ -355,16 +357,12 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(
     if (j < jhi) issue_tile(j + 1, st ^ 1);
 
     const int k0 = j * kBN;
+    // A tile outside this wave's key range (other waves of the workgroup need it) runs
+    // masked: every score is -inf, so it adds nothing and triggers no rescale.
     const bool relevant = wave_live && k0 <= kmax_w && k0 + kBN - 1 >= kmin_w;
-    if (relevant) {
-      const char* st_base = smem + st * T::STAGE;
-      const bool full = (!causal || k0 + kBN - 1 <= off + q0w) &&
-                        (window == 0 || off + qw_last - k0 < window) && (k0 + kBN <= Lk);
-      if (full)
-        tile_step(st_base, k0, std::false_type{});
-      else
-        tile_step(st_base, k0, std::true_type{});
-    }
+    const bool full = relevant && (!causal || k0 + kBN - 1 <= off + q0w) &&
+                      (window == 0 || off + qw_last - k0 < window) && (k0 + kBN <= Lk);
+    tile_step(smem + st * T::STAGE, k0, !full);
   }
 
   // ---- epilogue: O = O^T / l, bf16 RNE ---------------------------------------------------
