@@ -783,7 +783,7 @@ static int pow2_at_least(int g) {
   return p;
 }
 
-static int device_cus() {
+int device_cus() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||

@@ -84,6 +84,9 @@ struct PrefillPagedArgs {
 DecodePlan plan_decode(int B, int q_len, int Hq, int Hkv, int D, int max_context_len, int window,
                        int split_tokens);
 
+// Compute units of the current device (256 on MI355X if the query fails).
+int device_cus();
+
 int launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 int launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 int launch_decode(const DecodeArgs& a, hipStream_t stream);

@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int S,
     int Hq, int Hkv, int G, int HW, int QW, int n_qblk, int n_hsub, float scale_log2,
-    int causal, int window, PagedArgs pg) {
+    int causal, int window, int cpx, PagedArgs pg) {
   using T = PTile<D>;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
@@ -124,11 +124,18 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(
   // Consecutive workgroup ids are dispatched round-robin over the 8 XCDs, each with its own L2.
   // When the number of (b, kv head, head sub-group) groups is a multiple of 8, group gi runs
   // entirely on XCD gi % 8, so its K/V stream is fetched into one L2 and reused there; inside
-  // an XCD the query blocks still go longest first.
+  // an XCD the query blocks go longest first, dealt to the XCD's CUs in rounds of `cpx` slots
+  // whose direction alternates (round r takes ranks rC .. rC+C-1 forwards when r is even,
+  // backwards when odd). When the whole grid is resident at once, the CU that receives the
+  // longest block of one round receives the shortest of the next, so every CU's causal work
+  // sums to about the same.
   const int n_groups = gridDim.x / n_qblk;
   int gi, qblk_rank;
   if ((n_groups & 7) == 0) {
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int xcd = blockIdx.x & 7, slot0 = blockIdx.x >> 3;
+    const int round = slot0 / cpx, pos = slot0 % cpx;
+    const int len = min(cpx, (int)(gridDim.x >> 3) - round * cpx);  // last round may be short
+    const int slot = round * cpx + ((round & 1) ? len - 1 - pos : pos);
     const int per_xcd = n_groups >> 3;
     qblk_rank = slot / per_xcd;
     gi = xcd + 8 * (slot % per_xcd);
@@ -399,16 +406,18 @@ static void launch_d(const void* q, const void* k, const void* v, void* o, float
   const long long nwg = (long long)B * Hkv * n_hsub * n_qblk;
   const float scale_log2 = scale * kLog2e;
   const size_t lds = 2 * PTile<D>::STAGE;
+  // 64 KB of dynamic LDS at D=128 needs the opt-in; if it fails the launch fails and the
+  // entry point reports the launch error
   static bool attr_set = false;
-  if (!attr_set) {
-    hipFuncSetAttribute((const void*)prefill_bf16_kernel<D, PAGED>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    attr_set = true;
-  }
+  if (!attr_set)
+    attr_set = hipFuncSetAttribute((const void*)prefill_bf16_kernel<D, PAGED>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)lds) == hipSuccess;
+  const int cus = device_cus();
   hipLaunchKernelGGL((prefill_bf16_kernel<D, PAGED>), dim3((unsigned)nwg), dim3(kPrefillThreads),
                      lds, stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                      (uint16_t*)o, lse, S, Hq, Hkv, G, HW, QW, n_qblk, n_hsub, scale_log2, causal,
-                     window, pg);
+                     window, cus >= 16 ? cus / 8 : 1, pg);
 }
 
 int launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
