@@ -804,10 +804,13 @@ DecodePlan plan_decode(int B, int QL, int Hq, int Hkv, int D, int max_context_le
   const int ncol = (Hq / Hkv) * QL;  // query columns per (sequence, KV head)
   if (split_tokens == 0 && window == 0 && B <= kStreamMaxB) {
     // balanced shape (no window: context lengths, and so the work per sequence, can be
-    // arbitrarily ragged): at most one wave per list entry, and no more waves than the GPU
-    // holds at once (32 per CU for 256-thread workgroups)
+    // arbitrarily ragged): at most one wave per list entry and two 4-wave workgroups per CU.
+    // Every wave gets the same amount of work, so the workgroup count must be a whole multiple
+    // of the CU count; of 1, 2, 3, 4 and 8 workgroups per CU, 2 streams fastest (longer
+    // ranges per wave mean fewer partials to write and merge, and the 8 waves still keep
+    // enough loads in flight)
     const int64_t max_entries = (int64_t)B * Hkv * ((span + 15) / 16 + 1);
-    const int64_t waves = std::min<int64_t>((int64_t)device_cus() * 32, max_entries);
+    const int64_t waves = std::min<int64_t>((int64_t)device_cus() * 8, max_entries);
     p.stream = true;
     p.stream_waves_max = (int)std::max<int64_t>(kDecodeWaves, waves);
     const size_t slots = (size_t)B * Hkv + p.stream_waves_max;
