@@ -15,7 +15,8 @@
 // i < D/2 pairs with i + D/2 and the pair turns by pos * base^(-2i/D). The frequencies come
 // from an fp64 table built once per workgroup; the angle and its reduction modulo 2*pi are
 // fp64 (positions reach tens of thousands of radians); sin, cos and the rotation are fp32,
-// rounded to bf16 (RNE) when stored as bf16.
+// rounded to bf16 (RNE) when stored as bf16. Each (token, pair) angle is evaluated once per
+// workgroup and shared by the token's heads through LDS.
 //
 // HBM-bound elementwise work: one thread moves 8 elements (16 B of bf16 input); the D / 8
 // threads of one (token, head) row sit in adjacent lanes and reduce the row's absmax (and
@@ -34,21 +35,39 @@ __device__ __forceinline__ void rope_table(double* inv_freq, double base) {
   __syncthreads();
 }
 
-// Rotate the 8 values x (elements 8c .. 8c+7 of a D-wide row, c = lane's chunk) at position
-// pos. The partner half of the row sits TPR/2 lanes away; every lane of the row must call.
+// The angle of a pair depends only on (position, pair index), so a workgroup computes each
+// (token, pair) of its rows once: the first of its rows that belongs to a token fills that
+// token's (cos, sin) table in LDS, four pairs per lane (D/2 = 4 * TPR), and every row of the
+// token reads it after a barrier. Same arithmetic for every element as computing it in place.
 template <int D>
-__device__ __forceinline__ void rope8(float (&x)[8], int c, int pos, const double* inv_freq) {
+__device__ __forceinline__ void rope_fill(float2* __restrict__ row_cs, int c, int pos,
+                                          const double* inv_freq) {
   constexpr int TPR = D / 8;
   constexpr double kTwoPi = 6.283185307179586476925286766559;
-  const bool lo_half = c < TPR / 2;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float y = __shfl_xor(x[e], TPR / 2, TPR);  // element d +- D/2
-    const double ang = (double)pos * inv_freq[(8 * c + e) % (D / 2)];
+  for (int k = 0; k < 4; ++k) {
+    const int i = c + TPR * k;
+    const double ang = (double)pos * inv_freq[i];
     const float r = (float)(ang - kTwoPi * rint(ang * (1.0 / kTwoPi)));  // in [-pi, pi]
     float sn, cs;
     sincosf(r, &sn, &cs);
-    x[e] = lo_half ? fmaf(x[e], cs, -y * sn) : fmaf(y, sn, x[e] * cs);
+    row_cs[i] = make_float2(cs, sn);
+  }
+}
+
+// Rotate the 8 values x (elements 8c .. 8c+7 of a D-wide row, c = lane's chunk) with the
+// token's (cos, sin) table. The partner half of the row sits TPR/2 lanes away; every lane of
+// the row must call.
+template <int D>
+__device__ __forceinline__ void rope8(float (&x)[8], int c, const float2* __restrict__ row_cs) {
+  constexpr int TPR = D / 8;
+  const bool lo_half = c < TPR / 2;
+  const int i0 = (8 * c) % (D / 2);  // pairs i0 .. i0+7 (element d and d +- D/2 share one)
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float y = __shfl_xor(x[e], TPR / 2, TPR);  // element d +- D/2
+    const float2 t = row_cs[i0 + e];
+    x[e] = lo_half ? fmaf(x[e], t.x, -y * t.y) : fmaf(y, t.y, x[e] * t.x);
   }
 }
 
@@ -60,8 +79,10 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     __half* __restrict__ k_scale, __half* __restrict__ v_scale, int64_t rows, int Hkv, int bs,
     int num_seqs, int max_blocks, int num_blocks, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ ctx, double rope_base) {
-  constexpr int TPR = D / 8;  // threads per (token, head) row
+  constexpr int TPR = D / 8;        // threads per (token, head) row
+  constexpr int ROWS = 256 / TPR;   // rows per workgroup
   __shared__ double s_inv[ROPE ? D / 2 : 1];
+  __shared__ float2 s_cs[ROPE ? ROWS : 1][ROPE ? D / 2 : 1];
   if constexpr (ROPE) rope_table<D>(s_inv, rope_base);
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t row = gid / TPR;
@@ -98,12 +119,23 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
   }
   const int64_t src = r * D + c * 8;
   const int64_t dst = pool_offset(pb, Hkv, g, bs, slot, D) + c * 8;
+  u32x4 win[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+  if (in_range) {
+    win[0] = *reinterpret_cast<const u32x4*>(k_new + src);
+    win[1] = *reinterpret_cast<const u32x4*>(v_new + src);
+  }
+  int cs_row = 0;  // this row's token's table: its first row inside the workgroup
+  if constexpr (ROPE) {
+    const int64_t r0 = (int64_t)blockIdx.x * ROWS;
+    const int64_t first = t * Hkv > r0 ? t * Hkv : r0;
+    cs_row = (int)(first - r0);
+    if (in_range && r == first) rope_fill<D>(s_cs[cs_row], c, rpos, s_inv);
+    __syncthreads();
+  }
 
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
-    const uint16_t* in = which == 0 ? k_new : v_new;
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (in_range) w = *reinterpret_cast<const u32x4*>(in + src);
+    u32x4 w = win[which];
     const bool rot = ROPE && which == 0;  // RoPE turns K only
     float x[8];
 #pragma unroll
@@ -111,7 +143,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
       x[2 * i] = bf16_lo(w[i]);
       x[2 * i + 1] = bf16_hi(w[i]);
     }
-    if (rot) rope8<D>(x, c, rpos, s_inv);
+    if (rot) rope8<D>(x, c, s_cs[cs_row]);
     if constexpr (KV == kKvBf16) {
       uint16_t* out = reinterpret_cast<uint16_t*>(which == 0 ? k_cache : v_cache);
       if (rot) {
@@ -169,7 +201,9 @@ __global__ __launch_bounds__(256) void rope_rows_kernel(uint16_t* __restrict__ x
                                                         const int32_t* __restrict__ pos,
                                                         int64_t rows, int H, double rope_base) {
   constexpr int TPR = D / 8;
+  constexpr int ROWS = 256 / TPR;
   __shared__ double s_inv[D / 2];
+  __shared__ float2 s_cs[ROWS][D / 2];
   rope_table<D>(s_inv, rope_base);
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t row = gid / TPR;
@@ -179,13 +213,18 @@ __global__ __launch_bounds__(256) void rope_rows_kernel(uint16_t* __restrict__ x
   u32x4 w = {0u, 0u, 0u, 0u};
   uint16_t* p = x + r * D + 8 * c;
   if (in_range) w = *reinterpret_cast<const u32x4*>(p);
+  const int64_t t = r / H, r0 = (int64_t)blockIdx.x * ROWS;
+  const int64_t first = t * H > r0 ? t * H : r0;  // the token's first row in the workgroup
+  const int cs_row = (int)(first - r0);
+  if (in_range && r == first) rope_fill<D>(s_cs[cs_row], c, pos[t], s_inv);
+  __syncthreads();
   float v[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     v[2 * i] = bf16_lo(w[i]);
     v[2 * i + 1] = bf16_hi(w[i]);
   }
-  rope8<D>(v, c, in_range ? pos[r / H] : 0, s_inv);
+  rope8<D>(v, c, s_cs[cs_row]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
   if (in_range) *reinterpret_cast<u32x4*>(p) = w;
