@@ -4,6 +4,8 @@
 #include "launch.h"
 
 #include <cmath>
+#include <cstdint>
+#include <initializer_list>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -142,6 +144,9 @@ static int decode_impl(const char* who, const void* q, const void* k_cache, cons
     return fail(ATTN_ERR_NULL, "an int8 / fp8 cache needs k_scale and v_scale");
   if (kv_dtype == ATTN_BF16 && (k_scale || v_scale))
     return fail(ATTN_ERR_SHAPE, "k_scale/v_scale must be NULL for a bf16 cache");
+  for (const void* p : {q, k_cache, v_cache, k_scale, v_scale, (const void*)o})
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+      return fail(ATTN_ERR_SHAPE, "q, o, the caches and their scales must be 16-byte aligned");
   if (B < 1 || q_len < 1 || Hq < 1 || Hkv < 1 || max_blocks_per_seq < 1 || num_blocks < 1 ||
       max_context_len < 1)
     return fail(ATTN_ERR_SHAPE, "B, q_len, Hq, Hkv, max_blocks_per_seq, num_blocks, max_context_len must be >= 1");

@@ -35,6 +35,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One global_load_lds_dwordx4: each lane copies 16 bytes from `g` to LDS byte address
+// lds_off + 16 * lane. Written as asm so the compiler does not treat every later LDS read as
+// a possible alias of the in-flight copy (it would wait for the copy before unrelated LDS
+// reads); the caller awaits completion explicitly (vmcnt) before reading the data. The
+// instruction writes no registers.
+__device__ __forceinline__ void lds_dma_16(const void* g, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_off), "v"(g)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void*)p;
+}
+
 // 64-bit element offset of (block, head, slot, 0) in a [num_blocks][Hkv][bs][D] pool.
 __device__ __forceinline__ int64_t pool_offset(int pb, int Hkv, int g, int bs, int slot, int D) {
   return (((int64_t)pb * Hkv + g) * bs + slot) * (int64_t)D;

@@ -54,6 +54,9 @@ __device__ __forceinline__ int decode_ctx(const int32_t* ctx_lens, int b, int ma
   return c < 0 ? 0 : (c > cap ? cap : c);
 }
 
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_v2i32;
+
 // K/V cache reads are streamed once per call: non-temporal loads keep them from displacing
 // reusable lines (the table slice, Q) and measured faster on MI355X for pure streaming.
 template <typename V>
@@ -108,6 +111,7 @@ struct DecodeShape {
 // G heads of one (sequence, KV head). The LDS staging slices belong to the wave.
 template <int D, int GP, int KV>
 struct DecodeWave {
+  static constexpr bool kMfmaPv = false;
   using SH = DecodeShape<D, KV>;
   static constexpr bool BYTE = SH::BYTE, I8 = KV == kKvI8, F8 = KV == kKvFp8;
   static constexpr int BS = SH::BS, U = SH::U, CT = U * BS;  // CT tokens per chunk
@@ -198,7 +202,8 @@ struct DecodeWave {
   __device__ __forceinline__ void load(Chunk& c, const void* __restrict__ k_cache,
                                        const void* __restrict__ v_cache,
                                        const __half* __restrict__ k_scale,
-                                       const __half* __restrict__ v_scale, int Hkv, int g) {
+                                       const __half* __restrict__ v_scale, int Hkv, int g,
+                                       Lds&) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t brow = pool_offset(c.pb[u], Hkv, g, BS, 0, D);
@@ -422,9 +427,266 @@ struct DecodeWave {
         for (int e = 0; e < 8; ++e) acc[h][e] -= corr;
       }
     }
+  }
 
+  // f(column, d0, values) for each run of 8 consecutive d this lane holds (after reduce)
+  template <typename F>
+  __device__ __forceinline__ void emit(F&& f) const {
+    if (ts == 0) {
+#pragma unroll
+      for (int h = 0; h < GP; ++h) f(h, 8 * c8, acc[h]);
+    }
   }
 };
+
+// Byte caches (INT8, FP8 E4M3): the same per-wave state with PV on MFMA. A chunk is 32 tokens
+// (two 16-token blocks). Row m of block MFMA u (u = 0, 1) is chunk token 8*(m/4) + 4u + m%4,
+// so the score accumulator of lane (column c, group g) holds chunk tokens 8g .. 8g+7 -- the
+// B operand of v_mfma_f32_16x16x32_f16 with the 32 tokens as K. V codes go global -> LDS (the
+// wave's own slice, 16-byte chunks XOR-swizzled by row) and return transposed with
+// ds_read_b64_tr_b8: lane (d, g) of slice s receives tokens 8g .. 8g+7 of d = 16s + lane % 16,
+// widened to fp16 exactly as K is. Oᵀ accumulates in 16x16 tiles: lane (c, g) holds
+// d = 16s + 4g .. 4g+3 of column c.
+template <int D, int GP, int KV>
+struct DecodeWaveM {
+  static constexpr bool kMfmaPv = true;
+  static constexpr bool I8 = KV == kKvI8, F8 = KV == kKvFp8;
+  static_assert(I8 || F8, "byte caches only");
+  static constexpr int BS = 16, U = 2, CT = 32;  // CT tokens per chunk
+  static constexpr int KLOADS = D / 64;           // 16-byte K loads per lane per block MFMA
+  static constexpr int KSTEPS = D / 32;           // QK MFMA k-steps
+  static constexpr int NS = D / 16;               // 16-d output slices
+  static constexpr int VINSTR = CT * D / 1024;    // 1 KB DMA instructions per chunk
+  struct Lds {
+    __attribute__((aligned(16))) uint8_t v[CT * D];  // V codes, [token][16-byte chunk ^ swz]
+  };
+  // chunk swizzle of V row r: the 8 rows one transposing read touches land on distinct banks
+  static __device__ __forceinline__ int swz(int r) { return D == 128 ? (r & 7) : ((r >> 2) & 3); }
+
+  int lane, hq, grp;
+  f16x8 qf[KSTEPS];
+  float bias;     // INT8: 1152 * sum of this column's fp16 q values
+  float m_run;    // this lane's column, log2 units
+  float l_part;   // this lane's share of the column's row sum
+  float ps_part;  // INT8: this lane's share of sum(p'), in the fp16 values used
+  f32x4 o[NS];    // Oᵀ tiles
+  int qpos, wlo;
+
+  __device__ __forceinline__ void init(int lane_) {
+    lane = lane_;
+    hq = lane & 15;  // column (QK output, P operand, O tiles)
+    grp = lane >> 4;
+  }
+
+  // Q^T of the wave's columns, padded to 16 (same rule as DecodeWave): step j covers
+  // d = 64*(j/2) + 16*grp + 8*(j%2) + e.
+  __device__ __forceinline__ void load_q(const uint16_t* __restrict__ q, int b, int g, int G,
+                                         int QL, int Hq, int ctx, int window) {
+    float qsum = 0.f;
+    const int ncol = G * QL;
+    const int r = hq / G, h = hq % G;
+    const uint16_t* qrow = q + (((int64_t)b * QL + r) * Hq + g * G + h) * D;
+    qpos = ctx - QL + r;
+    wlo = window > 0 ? qpos - window + 1 : INT_MIN;
+#pragma unroll
+    for (int j = 0; j < KSTEPS; ++j) {
+      const int d0 = 64 * (j / 2) + 16 * grp + 8 * (j % 2);
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (hq < ncol) w = *reinterpret_cast<const u32x4*>(qrow + d0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qf[j][2 * e] = (_Float16)bf16_lo(w[e]);
+        qf[j][2 * e + 1] = (_Float16)bf16_hi(w[e]);
+        qsum += (float)qf[j][2 * e] + (float)qf[j][2 * e + 1];
+      }
+    }
+    if constexpr (I8) {
+      qsum += __shfl_xor(qsum, 16);
+      qsum = sum_x32(qsum);
+    }
+    bias = I8 ? kI8Bias * qsum : 0.f;
+  }
+
+  __device__ __forceinline__ void reset() {
+    m_run = kNegBig;
+    l_part = 0.f;
+    ps_part = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) o[s] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+
+  struct Chunk {
+    u32x4 kw[U][KLOADS];  // K codes of this lane's row of block MFMA u
+    u32x4 ksc8, vsc8;     // fp16 scales of chunk tokens 8*grp .. 8*grp+7
+    int pb[U];
+    bool okb[U];
+    int t0;
+  };
+  // physical block of chunk block i (0 or 1); a select, not an indexed access (a lane-varying
+  // index would put the array in scratch memory)
+  static __device__ __forceinline__ int blk_of(const Chunk& c, int i) { return i ? c.pb[1] : c.pb[0]; }
+
+  // Issue every load of a chunk (pb, okb and t0 already set): K codes and scales to
+  // registers, V codes to the wave's LDS slice (awaited in compute).
+  __device__ __forceinline__ void load(Chunk& c, const void* __restrict__ k_cache,
+                                       const void* __restrict__ v_cache,
+                                       const __half* __restrict__ k_scale,
+                                       const __half* __restrict__ v_scale, int Hkv, int g,
+                                       Lds& L) {
+    const int8_t* kb = reinterpret_cast<const int8_t*>(k_cache);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int tok = 8 * (hq >> 2) + 4 * u + (hq & 3);  // this lane's row of block MFMA u
+      const int8_t* kc = kb + pool_offset(blk_of(c, tok >> 4), Hkv, g, BS, tok & 15, D);
+#pragma unroll
+      for (int jj = 0; jj < KLOADS; ++jj) c.kw[u][jj] = ld_stream<u32x4>(kc + 64 * jj + 16 * grp);
+    }
+    const int64_t srow = ((int64_t)blk_of(c, grp >> 1) * Hkv + g) * BS + ((8 * grp) & 15);
+    c.ksc8 = *reinterpret_cast<const u32x4*>(k_scale + srow);
+    c.vsc8 = *reinterpret_cast<const u32x4*>(v_scale + srow);
+    const int8_t* vb = reinterpret_cast<const int8_t*>(v_cache);
+#pragma unroll
+    for (int n = 0; n < VINSTR; ++n) {
+      const int off = n * 1024 + 16 * lane;  // LDS byte of this lane's 16 bytes
+      const int r = off / D, ch = (off % D) / 16;
+      const int8_t* src = vb + pool_offset(blk_of(c, r >> 4), Hkv, g, BS, r & 15, D) + 16 * (ch ^ swz(r));
+      lds_dma_16(src, lds_addr(L.v + n * 1024));
+    }
+  }
+
+  // Online softmax + PV of a loaded chunk (tokens outside [lo, hi) masked, and for each column
+  // the tokens after its query position or left of its window).
+  __device__ __forceinline__ void compute(const Chunk& c, int lo, int hi, float scale_log2,
+                                          Lds& L) {
+    // ---- scores on MFMA (rows permuted: lane (column, grp) gets tokens 8grp + 4u + i) ------
+    float sc[U][4];
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jj = 0; jj < KLOADS; ++jj)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          u32x4 hv;
+          if constexpr (I8) {
+            const uint32_t w0 = c.kw[u][jj][2 * sub] ^ 0x80808080u;
+            const uint32_t w1 = c.kw[u][jj][2 * sub + 1] ^ 0x80808080u;
+            hv = (u32x4){widen_lo(w0), widen_hi(w0), widen_lo(w1), widen_hi(w1)};
+          } else {
+            const uint32_t w0 = c.kw[u][jj][2 * sub], w1 = c.kw[u][jj][2 * sub + 1];
+            hv = (u32x4){fp8x2_lo(w0), fp8x2_hi(w0), fp8x2_lo(w1), fp8x2_hi(w1)};
+          }
+          a4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, hv),
+                                                      qf[2 * jj + sub], a4, 0, 0, 0);
+        }
+      const bool okb = (grp >> 1) ? c.okb[1] : c.okb[0];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * u + i;  // token 8grp + e of the chunk
+        const int t = c.t0 + 8 * grp + e;
+        const bool vis = okb && t >= lo && t < hi && t <= qpos && t >= wlo;
+        const float ks = __half2float(__builtin_bit_cast(__half, (uint16_t)(c.ksc8[e >> 1] >> (16 * (e & 1)))));
+        float s;
+        if constexpr (I8)
+          s = (a4[i] - bias) * ks * scale_log2;
+        else
+          s = a4[i] * ks * scale_log2;
+        sc[u][i] = vis ? s : -INFINITY;
+        cmax = fmaxf(cmax, sc[u][i]);
+      }
+    }
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+    cmax = max_x32(cmax);
+    // lazy rescale: move the running max only when it grows by more than 8 (log2 units)
+    if (__builtin_amdgcn_ballot_w64(cmax > m_run + 8.0f) != 0) {
+      const float m_new = fmaxf(m_run, cmax);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_part *= alpha;
+      ps_part *= alpha;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) o[s] *= alpha;  // this lane's column
+    }
+    // ---- probabilities p' = p * v_scale (fp16): the B operand, tokens 8grp .. 8grp+7 -----
+    f16x8 pf;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * u + i;
+        const float p = fast_exp2(sc[u][i] - m_run);
+        l_part += p;
+        const float vs = __half2float(__builtin_bit_cast(__half, (uint16_t)(c.vsc8[e >> 1] >> (16 * (e & 1)))));
+        // masked tokens: p' = 0 exactly, and their (possibly NaN) scale is not used
+        const _Float16 pv16 = (_Float16)(sc[u][i] == -INFINITY ? 0.f : p * vs);
+        ps_part += (float)pv16;
+        pf[e] = pv16;
+      }
+    // ---- PV on MFMA ------------------------------------------------------------------------
+    // bytes of chunk tokens outside [lo, hi) or in an unusable block are zeroed before
+    // widening: their p' is 0, but unwritten slots may hold NaN codes (0 * NaN = NaN)
+    u32x2 vmask = {0xffffffffu, 0xffffffffu};
+    const bool ragged = !(c.okb[0] && c.okb[1] && c.t0 >= lo && c.t0 + CT <= hi);
+    if (ragged) {
+      const bool okb = (grp >> 1) ? c.okb[1] : c.okb[0];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int t = c.t0 + 8 * grp + e;
+        if (!(okb && t >= lo && t < hi)) vmask[e >> 2] &= ~(0xffu << (8 * (e & 3)));
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's V copy has landed in LDS
+    const int rr = 8 * grp + ((lane & 15) >> 1);  // the row this lane addresses
+    const int rbase = rr * D + 8 * (lane & 1);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const u32x2 raw = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                     (lds_v2i32*)(L.v + rbase + 16 * (s ^ swz(rr)))));
+      const uint32_t w0 = raw[0] & vmask[0], w1 = raw[1] & vmask[1];
+      u32x4 hv;
+      if constexpr (I8) {
+        const uint32_t x0 = w0 ^ 0x80808080u, x1 = w1 ^ 0x80808080u;
+        hv = (u32x4){widen_lo(x0), widen_hi(x0), widen_lo(x1), widen_hi(x1)};
+      } else {
+        hv = (u32x4){fp8x2_lo(w0), fp8x2_hi(w0), fp8x2_lo(w1), fp8x2_hi(w1)};
+      }
+      o[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, hv), pf, o[s], 0, 0, 0);
+    }
+  }
+
+  // Row sum l and sum(p') of this lane's column (complete on every lane of the column); the
+  // Oᵀ tiles are already complete, the INT8 bias is removed here.
+  __device__ __forceinline__ void reduce(float& l_w, float& ps_w) {
+    l_w = l_part + __shfl_xor(l_part, 16);
+    l_w = sum_x32(l_w);
+    ps_w = 0.f;
+    if constexpr (I8) {
+      ps_w = ps_part + __shfl_xor(ps_part, 16);
+      ps_w = sum_x32(ps_w);
+      const float corr = kI8Bias * ps_w;  // remove the +1152 of the codes
+#pragma unroll
+      for (int s = 0; s < NS; ++s) o[s] -= corr;
+    }
+  }
+
+  // f(column, d0, values) for each run of 4 consecutive d this lane holds (columns < GP)
+  template <typename F>
+  __device__ __forceinline__ void emit(F&& f) const {
+    if (hq < GP) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const float v4[4] = {o[s][0], o[s][1], o[s][2], o[s][3]};
+        f(hq, 16 * s + 4 * grp, v4);
+      }
+    }
+  }
+};
+
+template <int D, int GP, int KV>
+using DecodeWaveT = typename std::conditional<KV == kKvBf16, DecodeWave<D, GP, KV>,
+                                              DecodeWaveM<D, GP, KV>>::type;
 
 // ---- fixed split: one workgroup of 4 waves per (split, g, b) --------------------------------
 template <int D, int GP, int KV>
@@ -436,7 +698,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     float* __restrict__ part_o, float* __restrict__ part_lse, int Hq, int Hkv, int G, int QL,
     int max_blocks, int num_blocks, int max_ctx, float scale_log2, int window, int C,
     int n_split) {
-  using W = DecodeWave<D, GP, KV>;
+  using W = DecodeWaveT<D, GP, KV>;
   constexpr int BS = W::BS, U = W::U;
   __shared__ typename W::Lds s_lds[kDecodeWaves];
   __shared__ float s_red[kDecodeWaves][GP][D];
@@ -494,7 +756,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
       c.pb[u] = c.okb[u] ? e : 0;
     }
     c.t0 = t_begin + blk0 * BS;
-    w.load(c, k_cache, v_cache, k_scale, v_scale, Hkv, g);
+    w.load(c, k_cache, v_cache, k_scale, v_scale, Hkv, g, s_lds[wave]);
   };
   for (int ch = wave; ch < nchunk; ch += kDecodeWaves) {
     prep(cA, ch);
@@ -507,12 +769,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     s_ml[wave][0][w.hq] = w.m_run;
     s_ml[wave][1][w.hq] = l_w;
   }
-  if (w.ts == 0) {
+  w.emit([&](int h, int d0, const auto& v) {
+    constexpr int N = sizeof(v) / sizeof(v[0]);
 #pragma unroll
-    for (int h = 0; h < GP; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s_red[wave][h][8 * w.c8 + e] = w.acc[h][e];
-  }
+    for (int e = 0; e < N; ++e) s_red[wave][h][d0 + e] = v[e];
+  });
   __syncthreads();
 
   // ---- merge the 4 waves and write ---------------------------------------------------------
@@ -619,7 +880,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
     int32_t* __restrict__ prefix_out, float* __restrict__ part_o, float* __restrict__ part_lse,
     int B, int Hq, int Hkv, int G, int QL, int max_blocks, int num_blocks, int max_ctx,
     float scale_log2, int window) {
-  using W = DecodeWave<D, GP, KV>;
+  using W = DecodeWaveT<D, GP, KV>;
   constexpr int BS = W::BS, U = W::U;
   __shared__ typename W::Lds s_lds[kDecodeWaves];
   __shared__ int s_pre[kStreamMaxB + 1];
@@ -706,7 +967,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
         c.pb[u] = c.okb[u] ? e : 0;
       }
       c.t0 = (lb0 + j) * BS;
-      w.load(c, k_cache, v_cache, k_scale, v_scale, Hkv, g);
+      w.load(c, k_cache, v_cache, k_scale, v_scale, Hkv, g, s_lds[wave]);
     };
 
     w.load_q(q, b, g, G, QL, Hq, ctx, window);
@@ -720,27 +981,44 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
     const bool whole = j0 == 0 && j1 == nv;
     const int64_t slot = (int64_t)b * Hkv + g + p;
     const int ncol = G * QL;
+    // column h's row sum and max: lane h holds them (both lane layouts)
+    float lcol[GP], mcol[GP];
 #pragma unroll
-    for (int h = 0; h < GP; ++h) {  // column h: query row h / G, head g*G + h % G
-      const float lh = __shfl(l_w, h), mh = __shfl(w.m_run, h);
-      if (h < ncol && w.ts == 0) {
-        const float inv = lh > 0.f ? 1.0f / lh : 0.f;
-        if (whole) {
-          u32x4 o4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o4[e] = pack_bf16x2(w.acc[h][2 * e] * inv, w.acc[h][2 * e + 1] * inv);
-          const int64_t orow = ((int64_t)b * QL + h / G) * Hq + g * G + h % G;
-          *reinterpret_cast<u32x4*>(out + orow * D + 8 * w.c8) = o4;
-        } else {
-          float* po = part_o + ((slot * ncol + h) * D + 8 * w.c8);
-          f32x4 a = {w.acc[h][0] * inv, w.acc[h][1] * inv, w.acc[h][2] * inv, w.acc[h][3] * inv};
-          f32x4 c = {w.acc[h][4] * inv, w.acc[h][5] * inv, w.acc[h][6] * inv, w.acc[h][7] * inv};
-          *reinterpret_cast<f32x4*>(po) = a;
-          *reinterpret_cast<f32x4*>(po + 4) = c;
-          if (w.c8 == 0) part_lse[slot * ncol + h] = lh > 0.f ? mh + __log2f(lh) : -INFINITY;
-        }
-      }
+    for (int h = 0; h < GP; ++h) {
+      lcol[h] = __shfl(l_w, h);
+      mcol[h] = __shfl(w.m_run, h);
     }
+    // column h: query row h / G, head g*G + h % G; v holds d0 .. d0 + N - 1
+    w.emit([&](int h, int d0, const auto& v) {
+      constexpr int N = sizeof(v) / sizeof(v[0]);
+      if (h >= ncol) return;
+      float lh, mh;
+      if constexpr (W::kMfmaPv) {  // h is this lane's own column
+        lh = l_w;
+        mh = w.m_run;
+      } else {
+        lh = lcol[h];
+        mh = mcol[h];
+      }
+      const float inv = lh > 0.f ? 1.0f / lh : 0.f;
+      if (whole) {
+        uint32_t o2[N / 2];
+#pragma unroll
+        for (int e = 0; e < N / 2; ++e) o2[e] = pack_bf16x2(v[2 * e] * inv, v[2 * e + 1] * inv);
+        const int64_t orow = ((int64_t)b * QL + h / G) * Hq + g * G + h % G;
+        uint16_t* dst = out + orow * D + d0;
+        if constexpr (N == 8)
+          *reinterpret_cast<u32x4*>(dst) = (u32x4){o2[0], o2[1], o2[2], o2[3]};
+        else
+          *reinterpret_cast<u32x2*>(dst) = (u32x2){o2[0], o2[1]};
+      } else {
+        float* po = part_o + ((slot * ncol + h) * D + d0);
+#pragma unroll
+        for (int e = 0; e < N; e += 4)
+          *reinterpret_cast<f32x4*>(po + e) = (f32x4){v[e] * inv, v[e + 1] * inv, v[e + 2] * inv, v[e + 3] * inv};
+        if (d0 == 0) part_lse[slot * ncol + h] = lh > 0.f ? mh + __log2f(lh) : -INFINITY;
+      }
+    });
     pos = pend;
     if (pos >= end) break;
     if (++g == Hkv) {  // next sequence with visible blocks (one exists: pos < T)

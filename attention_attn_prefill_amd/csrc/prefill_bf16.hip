@@ -55,23 +55,8 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
 typedef short i16x4 __attribute__((vector_size(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-// One global_load_lds_dwordx4: each lane copies 16 bytes from `g` to LDS byte address
-// lds_off + 16 * lane. Written as asm so the compiler does not treat every later LDS read as
-// a possible alias of the in-flight copy (it would wait for the copy before the current
-// tile's reads); completion is awaited explicitly with vmcnt(0) before the next barrier. The
-// instruction writes no registers.
-__device__ __forceinline__ void lds_dma_16(const void* g, uint32_t lds_off) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_off), "v"(g)
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const lds_void*)p;
-}
 
 template <int D>
 struct PTile {

@@ -152,7 +152,9 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_context
  *  workspace    : device buffer of at least attn_decode_workspace_size(...) bytes (may be NULL
  *                 when that size is 0); overwritten by the call; its contents on entry do not
  *                 matter. Two calls in flight at once must not share a workspace.
- *  Requirements: D in {64, 128}; block_size == 16; Hq % Hkv == 0 and Hq / Hkv <= 16.
+ *  Requirements: D in {64, 128}; block_size == 16; Hq % Hkv == 0 and Hq / Hkv <= 16;
+ *                 q, o, k_cache, v_cache, k_scale and v_scale 16-byte aligned (else
+ *                 ATTN_ERR_SHAPE).
  */
 int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       const void* k_scale, const void* v_scale,

@@ -86,6 +86,10 @@ def _decode(**kw):
     (dict(Hq=34, Hkv=2), A.ATTN_ERR_UNSUPPORTED), (dict(split=8208), A.ATTN_ERR_UNSUPPORTED),
     (dict(maxctx=5000, split=64), A.ATTN_ERR_WORKSPACE),
     (dict(maxctx=5000, split=64, ws=FAKE, wsb=16), A.ATTN_ERR_WORKSPACE),
+    # every tensor the kernels read or write in 16-byte pieces must be 16-byte aligned
+    (dict(q=ctypes.c_void_p(0x1008)), A.ATTN_ERR_SHAPE), (dict(o=ctypes.c_void_p(0x1004)), A.ATTN_ERR_SHAPE),
+    (dict(kc=ctypes.c_void_p(0x1002)), A.ATTN_ERR_SHAPE),
+    (dict(kv=A.ATTN_I8, ks=FAKE, vs=ctypes.c_void_p(0x1002)), A.ATTN_ERR_SHAPE),
 ])
 def test_decode_validation(kw, code):
     assert _decode(**kw) == code
@@ -107,6 +111,7 @@ def _multi(**kw):
     (dict(ql=5), A.ATTN_ERR_UNSUPPORTED),               # 4 heads per KV head x 5 rows > 16
     (dict(Hq=16, Hkv=1, ql=2), A.ATTN_ERR_UNSUPPORTED), (dict(B=40000), A.ATTN_ERR_SHAPE),
     (dict(), A.ATTN_ERR_WORKSPACE),                     # the balanced shape stages partials
+    (dict(kv=A.ATTN_FP8, ks=ctypes.c_void_p(0x1008), vs=FAKE), A.ATTN_ERR_SHAPE),
 ])
 def test_decode_multi_validation(kw, code):
     assert _multi(**kw) == code

@@ -142,3 +142,31 @@ def test_fp8_decode_70b_b16_sampled():
     assert np.array_equal(ks[probe].cpu().numpy().view(np.uint16), ksc.view(np.uint16))
     for b, ro in _oracle_sampled(wl, qf, table, ctx, [0, 9], lambda blk: quantized(blk)[:2]):
         assert maxabs(o[b], ro) <= BF16_TOL
+
+
+@pytest.mark.parametrize("split", [0, 32])
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp8_decode_ignores_nan_in_unwritten_slots(D, split):
+    """Slots after a sequence's last token are never written, so they may hold any byte: fill
+    them with E4M3 NaN codes (0x7F, 0xFF) and NaN scales. Their probabilities are 0, and the
+    result must still match the oracle, which reads only visible tokens."""
+    import attention_attn_prefill_amd as A
+    wl, ctx, table, qbits, qf, kc, ks, vc, vs = _small(D, 16, 4, 0, (1, 15, 17, 100, 333), 5400 + D)
+    kc, vc, ks, vs = kc.copy(), vc.copy(), ks.copy(), vs.copy()
+    for b, n in enumerate(ctx):
+        if n % 16:
+            pb = table[b, (n - 1) // 16]
+            kc[pb, :, n % 16:, :] = 0x7F
+            vc[pb, :, n % 16:, :] = 0xFF
+            ks[pb, :, n % 16:] = np.float16(np.nan)
+            vs[pb, :, n % 16:] = np.float16(np.nan)
+    o = A.attn_decode_paged(dev_bf16(qbits), dev(kc), dev(vc), dev(table), dev(ctx), int(ctx.max()),
+                            k_scale=dev(ks), v_scale=dev(vs), scale=wl.scale, split_tokens=split)
+    torch().cuda.synchronize()
+    o = host_f64(o)
+    assert np.isfinite(o).all()
+    visible = lambda c, s: oracle.dequantize_fp8(c, s)  # noqa: E731 -- NaN slots are never read
+    ro, _ = oracle.decode_paged(qf, visible(kc, np.nan_to_num(ks)), visible(vc, np.nan_to_num(vs)), table, ctx,
+                                wl.scale, 16, 0)
+    assert np.isfinite(ro).all()  # the oracle reads visible tokens only
+    assert maxabs(o, ro) <= BF16_TOL
