@@ -238,7 +238,7 @@ struct DecodeWave {
   // Online softmax + PV of a loaded chunk; tokens outside [lo, hi) are masked, and for each
   // column the tokens after its query position or left of its window.
   __device__ __forceinline__ void compute(const Chunk& c, int lo, int hi, float scale_log2,
-                                          Lds& L) {
+                                          Lds& L, bool = false) {
     // ---- scores on MFMA -----------------------------------------------------------------
     float sc[U][4];
     float cmax = -INFINITY;
@@ -457,6 +457,8 @@ struct DecodeWaveM {
   static constexpr int KSTEPS = D / 32;           // QK MFMA k-steps
   static constexpr int NS = D / 16;               // 16-d output slices
   static constexpr int VINSTR = CT * D / 1024;    // 1 KB DMA instructions per chunk
+  static constexpr int kLoads = U * KLOADS + 2 + VINSTR;  // vector memory ops load() issues
+  static_assert(kLoads < 64, "vmcnt field");
   struct Lds {
     __attribute__((aligned(16))) uint8_t v[CT * D];  // V codes, [token][16-byte chunk ^ swz]
   };
@@ -556,8 +558,9 @@ struct DecodeWaveM {
 
   // Online softmax + PV of a loaded chunk (tokens outside [lo, hi) masked, and for each column
   // the tokens after its query position or left of its window).
+  // next_in_flight: the next chunk's loads were issued after this chunk's (kLoads of them)
   __device__ __forceinline__ void compute(const Chunk& c, int lo, int hi, float scale_log2,
-                                          Lds& L) {
+                                          Lds& L, bool next_in_flight = false) {
     // ---- scores on MFMA (rows permuted: lane (column, grp) gets tokens 8grp + 4u + i) ------
     float sc[U][4];
     float cmax = -INFINITY;
@@ -636,7 +639,11 @@ struct DecodeWaveM {
         if (!(okb && t >= lo && t < hi)) vmask[e >> 2] &= ~(0xffu << (8 * (e & 3)));
       }
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's V copy has landed in LDS
+    // this chunk's V copy has landed in LDS (the next chunk's loads may stay in flight)
+    if (next_in_flight)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (kLoads & 0xF) | ((kLoads >> 4) << 14));
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);
     const int rr = 8 * grp + ((lane & 15) >> 1);  // the row this lane addresses
     const int rbase = rr * D + 8 * (lane & 1);
 #pragma unroll
@@ -882,7 +889,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
     float scale_log2, int window) {
   using W = DecodeWaveT<D, GP, KV>;
   constexpr int BS = W::BS, U = W::U;
-  __shared__ typename W::Lds s_lds[kDecodeWaves];
+  constexpr int NSLOT = W::kMfmaPv ? 2 : 1;  // byte caches: the next chunk's V lands in slot 1
+  __shared__ typename W::Lds s_lds[kDecodeWaves][NSLOT];
   __shared__ int s_pre[kStreamMaxB + 1];
   __shared__ int s_scan[kDecodeThreads];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -952,7 +960,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
     int win = j0;
     int tab = j0 + lane < j1 ? trow[j0 + lane] : -1;
     typename W::Chunk cA;
-    auto prep = [&](typename W::Chunk& c, int j) {
+    auto prep = [&](typename W::Chunk& c, int j, int slot) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         int e = -1;
@@ -967,14 +975,29 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
         c.pb[u] = c.okb[u] ? e : 0;
       }
       c.t0 = (lb0 + j) * BS;
-      w.load(c, k_cache, v_cache, k_scale, v_scale, Hkv, g, s_lds[wave]);
+      w.load(c, k_cache, v_cache, k_scale, v_scale, Hkv, g, s_lds[wave][slot]);
     };
 
     w.load_q(q, b, g, G, QL, Hq, ctx, window);
     w.reset();
-    for (int j = j0; j < j1; j += U) {
-      prep(cA, j);
-      w.compute(cA, lo, hi, scale_log2, s_lds[wave]);
+    if constexpr (W::kMfmaPv) {
+      // two chunks in flight: the next chunk's loads are issued before this one is computed
+      typename W::Chunk cB;
+      if (j0 < j1) prep(cA, j0, 0);
+      for (int j = j0; j < j1; j += 2 * U) {
+        const bool nb = j + U < j1;
+        if (nb) prep(cB, j + U, 1);
+        w.compute(cA, lo, hi, scale_log2, s_lds[wave][0], nb);
+        if (!nb) break;
+        const bool na = j + 2 * U < j1;
+        if (na) prep(cA, j + 2 * U, 0);
+        w.compute(cB, lo, hi, scale_log2, s_lds[wave][1], na);
+      }
+    } else {
+      for (int j = j0; j < j1; j += U) {
+        prep(cA, j, 0);
+        w.compute(cA, lo, hi, scale_log2, s_lds[wave][0]);
+      }
     }
     float l_w, ps_w;
     w.reduce(l_w, ps_w);
