@@ -54,6 +54,8 @@ __device__ __forceinline__ int decode_ctx(const int32_t* ctx_lens, int b, int ma
   return c < 0 ? 0 : (c > cap ? cap : c);
 }
 
+typedef short i16x4 __attribute__((vector_size(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2 lds_v2i32;
 
@@ -439,34 +441,41 @@ struct DecodeWave {
   }
 };
 
-// Byte caches (INT8, FP8 E4M3): the same per-wave state with PV on MFMA. A chunk is 32 tokens
-// (two 16-token blocks). Row m of block MFMA u (u = 0, 1) is chunk token 8*(m/4) + 4u + m%4,
-// so the score accumulator of lane (column c, group g) holds chunk tokens 8g .. 8g+7 -- the
-// B operand of v_mfma_f32_16x16x32_f16 with the 32 tokens as K. V codes go global -> LDS (the
-// wave's own slice, 16-byte chunks XOR-swizzled by row) and return transposed with
-// ds_read_b64_tr_b8: lane (d, g) of slice s receives tokens 8g .. 8g+7 of d = 16s + lane % 16,
-// widened to fp16 exactly as K is. Oᵀ accumulates in 16x16 tiles: lane (c, g) holds
+// PV on MFMA (byte caches, and bf16 caches with 8 or more query columns): the same per-wave
+// state as DecodeWave. A chunk is 32 tokens (two 16-token blocks). Row m of block MFMA u
+// (u = 0, 1) is chunk token 8*(m/4) + 4u + m%4, so the score accumulator of lane (column c,
+// group g) holds chunk tokens 8g .. 8g+7 -- the B operand of a 16x16x32 MFMA with the 32
+// tokens as K. V goes global -> LDS (the wave's own slice, 16-byte chunks XOR-swizzled by row)
+// and returns transposed: for byte caches ds_read_b64_tr_b8 gives lane (d, g) of slice s tokens
+// 8g .. 8g+7 of d = 16s + lane % 16 (widened to fp16 exactly as K is); for bf16 two
+// ds_read_b64_tr_b16 give 4 tokens each. Oᵀ accumulates in 16x16 tiles: lane (c, g) holds
 // d = 16s + 4g .. 4g+3 of column c.
 template <int D, int GP, int KV>
 struct DecodeWaveM {
   static constexpr bool kMfmaPv = true;
-  static constexpr bool I8 = KV == kKvI8, F8 = KV == kKvFp8;
-  static_assert(I8 || F8, "byte caches only");
+  static constexpr bool I8 = KV == kKvI8, F8 = KV == kKvFp8, BF = KV == kKvBf16;
+  static constexpr int ES = BF ? 2 : 1;           // bytes per cached element
   static constexpr int BS = 16, U = 2, CT = 32;  // CT tokens per chunk
-  static constexpr int KLOADS = D / 64;           // 16-byte K loads per lane per block MFMA
+  static constexpr int KLOADS = BF ? D / 32 : D / 64;  // 16-byte K loads per lane per block MFMA
   static constexpr int KSTEPS = D / 32;           // QK MFMA k-steps
   static constexpr int NS = D / 16;               // 16-d output slices
-  static constexpr int VINSTR = CT * D / 1024;    // 1 KB DMA instructions per chunk
-  static constexpr int kLoads = U * KLOADS + 2 + VINSTR;  // vector memory ops load() issues
+  static constexpr int ROWB = D * ES;             // bytes per V row
+  static constexpr int VINSTR = CT * ROWB / 1024;  // 1 KB DMA instructions per chunk
+  static constexpr int kLoads = U * KLOADS + (BF ? 0 : 2) + VINSTR;  // vector memory ops of load()
   static_assert(kLoads < 64, "vmcnt field");
+  typedef typename std::conditional<BF, bf16x8, f16x8>::type frag_t;
   struct Lds {
-    __attribute__((aligned(16))) uint8_t v[CT * D];  // V codes, [token][16-byte chunk ^ swz]
+    __attribute__((aligned(16))) uint8_t v[CT * ROWB];  // V, [token][16-byte chunk ^ swz]
   };
-  // chunk swizzle of V row r: the 8 rows one transposing read touches land on distinct banks
-  static __device__ __forceinline__ int swz(int r) { return D == 128 ? (r & 7) : ((r >> 2) & 3); }
+  // chunk swizzle of V row r: the rows one transposing read touches land on distinct banks
+  // (bf16: an even XOR keeps the two chunks of a 32-byte read segment together)
+  static __device__ __forceinline__ int swz(int r) {
+    if constexpr (BF) return D == 128 ? 2 * (r & 3) : 2 * ((r >> 1) & 1);
+    return D == 128 ? (r & 7) : ((r >> 2) & 3);
+  }
 
   int lane, hq, grp;
-  f16x8 qf[KSTEPS];
+  frag_t qf[KSTEPS];
   float bias;     // INT8: 1152 * sum of this column's fp16 q values
   float m_run;    // this lane's column, log2 units
   float l_part;   // this lane's share of the column's row sum
@@ -480,8 +489,8 @@ struct DecodeWaveM {
     grp = lane >> 4;
   }
 
-  // Q^T of the wave's columns, padded to 16 (same rule as DecodeWave): step j covers
-  // d = 64*(j/2) + 16*grp + 8*(j%2) + e.
+  // Q^T of the wave's columns, padded to 16 (same rule as DecodeWave): bf16 step j covers
+  // d = 32j + 8*grp + e; byte caches d = 64*(j/2) + 16*grp + 8*(j%2) + e.
   __device__ __forceinline__ void load_q(const uint16_t* __restrict__ q, int b, int g, int G,
                                          int QL, int Hq, int ctx, int window) {
     float qsum = 0.f;
@@ -492,14 +501,18 @@ struct DecodeWaveM {
     wlo = window > 0 ? qpos - window + 1 : INT_MIN;
 #pragma unroll
     for (int j = 0; j < KSTEPS; ++j) {
-      const int d0 = 64 * (j / 2) + 16 * grp + 8 * (j % 2);
+      const int d0 = BF ? 32 * j + 8 * grp : 64 * (j / 2) + 16 * grp + 8 * (j % 2);
       u32x4 w = {0u, 0u, 0u, 0u};
       if (hq < ncol) w = *reinterpret_cast<const u32x4*>(qrow + d0);
+      if constexpr (BF) {
+        qf[j] = __builtin_bit_cast(bf16x8, w);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qf[j][2 * e] = (_Float16)bf16_lo(w[e]);
-        qf[j][2 * e + 1] = (_Float16)bf16_hi(w[e]);
-        qsum += (float)qf[j][2 * e] + (float)qf[j][2 * e + 1];
+        for (int e = 0; e < 4; ++e) {
+          qf[j][2 * e] = (_Float16)bf16_lo(w[e]);
+          qf[j][2 * e + 1] = (_Float16)bf16_hi(w[e]);
+          qsum += (float)qf[j][2 * e] + (float)qf[j][2 * e + 1];
+        }
       }
     }
     if constexpr (I8) {
@@ -518,8 +531,8 @@ struct DecodeWaveM {
   }
 
   struct Chunk {
-    u32x4 kw[U][KLOADS];  // K codes of this lane's row of block MFMA u
-    u32x4 ksc8, vsc8;     // fp16 scales of chunk tokens 8*grp .. 8*grp+7
+    u32x4 kw[U][KLOADS];  // K of this lane's row of block MFMA u
+    u32x4 ksc8, vsc8;     // byte caches: fp16 scales of chunk tokens 8*grp .. 8*grp+7
     int pb[U];
     bool okb[U];
     int t0;
@@ -528,73 +541,87 @@ struct DecodeWaveM {
   // index would put the array in scratch memory)
   static __device__ __forceinline__ int blk_of(const Chunk& c, int i) { return i ? c.pb[1] : c.pb[0]; }
 
-  // Issue every load of a chunk (pb, okb and t0 already set): K codes and scales to
-  // registers, V codes to the wave's LDS slice (awaited in compute).
+  // Issue every load of a chunk (pb, okb and t0 already set): K (and scales) to registers,
+  // V to the wave's LDS slice (awaited in compute).
   __device__ __forceinline__ void load(Chunk& c, const void* __restrict__ k_cache,
                                        const void* __restrict__ v_cache,
                                        const __half* __restrict__ k_scale,
                                        const __half* __restrict__ v_scale, int Hkv, int g,
                                        Lds& L) {
-    const int8_t* kb = reinterpret_cast<const int8_t*>(k_cache);
+    const char* kb = reinterpret_cast<const char*>(k_cache);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int tok = 8 * (hq >> 2) + 4 * u + (hq & 3);  // this lane's row of block MFMA u
-      const int8_t* kc = kb + pool_offset(blk_of(c, tok >> 4), Hkv, g, BS, tok & 15, D);
+      const char* kc = kb + pool_offset(blk_of(c, tok >> 4), Hkv, g, BS, tok & 15, D) * ES;
 #pragma unroll
-      for (int jj = 0; jj < KLOADS; ++jj) c.kw[u][jj] = ld_stream<u32x4>(kc + 64 * jj + 16 * grp);
+      for (int j = 0; j < KLOADS; ++j)
+        c.kw[u][j] = ld_stream<u32x4>(kc + (BF ? 2 * (32 * j + 8 * grp) : 64 * j + 16 * grp));
     }
-    const int64_t srow = ((int64_t)blk_of(c, grp >> 1) * Hkv + g) * BS + ((8 * grp) & 15);
-    c.ksc8 = *reinterpret_cast<const u32x4*>(k_scale + srow);
-    c.vsc8 = *reinterpret_cast<const u32x4*>(v_scale + srow);
-    const int8_t* vb = reinterpret_cast<const int8_t*>(v_cache);
+    if constexpr (!BF) {
+      const int64_t srow = ((int64_t)blk_of(c, grp >> 1) * Hkv + g) * BS + ((8 * grp) & 15);
+      c.ksc8 = *reinterpret_cast<const u32x4*>(k_scale + srow);
+      c.vsc8 = *reinterpret_cast<const u32x4*>(v_scale + srow);
+    }
+    const char* vb = reinterpret_cast<const char*>(v_cache);
 #pragma unroll
     for (int n = 0; n < VINSTR; ++n) {
       const int off = n * 1024 + 16 * lane;  // LDS byte of this lane's 16 bytes
-      const int r = off / D, ch = (off % D) / 16;
-      const int8_t* src = vb + pool_offset(blk_of(c, r >> 4), Hkv, g, BS, r & 15, D) + 16 * (ch ^ swz(r));
+      const int r = off / ROWB, ch = (off % ROWB) / 16;
+      const char* src = vb + pool_offset(blk_of(c, r >> 4), Hkv, g, BS, r & 15, D) * ES + 16 * (ch ^ swz(r));
       lds_dma_16(src, lds_addr(L.v + n * 1024));
     }
   }
 
+  __device__ __forceinline__ float scale_of(u32x4 s8, int e) const {
+    return __half2float(__builtin_bit_cast(__half, (uint16_t)(s8[e >> 1] >> (16 * (e & 1)))));
+  }
+
   // Online softmax + PV of a loaded chunk (tokens outside [lo, hi) masked, and for each column
-  // the tokens after its query position or left of its window).
-  // next_in_flight: the next chunk's loads were issued after this chunk's (kLoads of them)
+  // the tokens after its query position or left of its window). next_in_flight: the next
+  // chunk's loads (kLoads of them) were issued after this chunk's.
   __device__ __forceinline__ void compute(const Chunk& c, int lo, int hi, float scale_log2,
                                           Lds& L, bool next_in_flight = false) {
     // ---- scores on MFMA (rows permuted: lane (column, grp) gets tokens 8grp + 4u + i) ------
     float sc[U][4];
     float cmax = -INFINITY;
+    const bool okb = (grp >> 1) ? c.okb[1] : c.okb[0];  // the block of tokens 8grp .. 8grp+7
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (BF) {
 #pragma unroll
-      for (int jj = 0; jj < KLOADS; ++jj)
+        for (int j = 0; j < KSTEPS; ++j)
+          a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, c.kw[u][j]), qf[j], a4, 0, 0, 0);
+      } else {
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-          u32x4 hv;
-          if constexpr (I8) {
-            const uint32_t w0 = c.kw[u][jj][2 * sub] ^ 0x80808080u;
-            const uint32_t w1 = c.kw[u][jj][2 * sub + 1] ^ 0x80808080u;
-            hv = (u32x4){widen_lo(w0), widen_hi(w0), widen_lo(w1), widen_hi(w1)};
-          } else {
-            const uint32_t w0 = c.kw[u][jj][2 * sub], w1 = c.kw[u][jj][2 * sub + 1];
-            hv = (u32x4){fp8x2_lo(w0), fp8x2_hi(w0), fp8x2_lo(w1), fp8x2_hi(w1)};
+        for (int jj = 0; jj < KLOADS; ++jj)
+#pragma unroll
+          for (int sub = 0; sub < 2; ++sub) {
+            u32x4 hv;
+            if constexpr (I8) {
+              const uint32_t w0 = c.kw[u][jj][2 * sub] ^ 0x80808080u;
+              const uint32_t w1 = c.kw[u][jj][2 * sub + 1] ^ 0x80808080u;
+              hv = (u32x4){widen_lo(w0), widen_hi(w0), widen_lo(w1), widen_hi(w1)};
+            } else {
+              const uint32_t w0 = c.kw[u][jj][2 * sub], w1 = c.kw[u][jj][2 * sub + 1];
+              hv = (u32x4){fp8x2_lo(w0), fp8x2_hi(w0), fp8x2_lo(w1), fp8x2_hi(w1)};
+            }
+            a4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, hv),
+                                                        qf[2 * jj + sub], a4, 0, 0, 0);
           }
-          a4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, hv),
-                                                      qf[2 * jj + sub], a4, 0, 0, 0);
-        }
-      const bool okb = (grp >> 1) ? c.okb[1] : c.okb[0];
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = 4 * u + i;  // token 8grp + e of the chunk
         const int t = c.t0 + 8 * grp + e;
         const bool vis = okb && t >= lo && t < hi && t <= qpos && t >= wlo;
-        const float ks = __half2float(__builtin_bit_cast(__half, (uint16_t)(c.ksc8[e >> 1] >> (16 * (e & 1)))));
         float s;
         if constexpr (I8)
-          s = (a4[i] - bias) * ks * scale_log2;
+          s = (a4[i] - bias) * scale_of(c.ksc8, e) * scale_log2;
+        else if constexpr (F8)
+          s = a4[i] * scale_of(c.ksc8, e) * scale_log2;
         else
-          s = a4[i] * ks * scale_log2;
+          s = a4[i] * scale_log2;
         sc[u][i] = vis ? s : -INFINITY;
         cmax = fmaxf(cmax, sc[u][i]);
       }
@@ -611,55 +638,86 @@ struct DecodeWaveM {
 #pragma unroll
       for (int s = 0; s < NS; ++s) o[s] *= alpha;  // this lane's column
     }
-    // ---- probabilities p' = p * v_scale (fp16): the B operand, tokens 8grp .. 8grp+7 -----
-    f16x8 pf;
+    // ---- probabilities: the B operand, tokens 8grp .. 8grp+7 -------------------------------
+    // bf16: p rounded to bf16, and the row sum adds the rounded values (those PV uses);
+    // byte caches: p' = p * v_scale in fp16
+    frag_t pf;
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = 4 * u + i;
         const float p = fast_exp2(sc[u][i] - m_run);
-        l_part += p;
-        const float vs = __half2float(__builtin_bit_cast(__half, (uint16_t)(c.vsc8[e >> 1] >> (16 * (e & 1)))));
-        // masked tokens: p' = 0 exactly, and their (possibly NaN) scale is not used
-        const _Float16 pv16 = (_Float16)(sc[u][i] == -INFINITY ? 0.f : p * vs);
-        ps_part += (float)pv16;
-        pf[e] = pv16;
+        if constexpr (BF) {
+          const __bf16 pb16 = (__bf16)p;
+          l_part += (float)pb16;
+          pf[e] = pb16;
+        } else {
+          l_part += p;
+          // masked tokens: p' = 0 exactly, and their (possibly NaN) scale is not used
+          const _Float16 pv16 = (_Float16)(sc[u][i] == -INFINITY ? 0.f : p * scale_of(c.vsc8, e));
+          ps_part += (float)pv16;
+          pf[e] = pv16;
+        }
       }
     // ---- PV on MFMA ------------------------------------------------------------------------
-    // bytes of chunk tokens outside [lo, hi) or in an unusable block are zeroed before
-    // widening: their p' is 0, but unwritten slots may hold NaN codes (0 * NaN = NaN)
-    u32x2 vmask = {0xffffffffu, 0xffffffffu};
+    // V of chunk tokens outside [lo, hi) or in an unusable block is zeroed: their p is 0, but
+    // unwritten slots may hold NaN (0 * NaN = NaN). Lane bits: token 8grp + e is byte e (byte
+    // caches) or half e of the two-read bf16 operand.
+    u32x4 vmask = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
     const bool ragged = !(c.okb[0] && c.okb[1] && c.t0 >= lo && c.t0 + CT <= hi);
     if (ragged) {
-      const bool okb = (grp >> 1) ? c.okb[1] : c.okb[0];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int t = c.t0 + 8 * grp + e;
-        if (!(okb && t >= lo && t < hi)) vmask[e >> 2] &= ~(0xffu << (8 * (e & 3)));
+        if (!(okb && t >= lo && t < hi)) {
+          if constexpr (BF)
+            vmask[e >> 1] &= ~(0xffffu << (16 * (e & 1)));
+          else
+            vmask[e >> 2] &= ~(0xffu << (8 * (e & 3)));
+        }
       }
     }
-    // this chunk's V copy has landed in LDS (the next chunk's loads may stay in flight)
     if (next_in_flight)
       __builtin_amdgcn_s_waitcnt(0x0F70 | (kLoads & 0xF) | ((kLoads >> 4) << 14));
     else
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-    const int rr = 8 * grp + ((lane & 15) >> 1);  // the row this lane addresses
-    const int rbase = rr * D + 8 * (lane & 1);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // this chunk's V copy has landed in LDS
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const u32x2 raw = __builtin_bit_cast(
-          u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                     (lds_v2i32*)(L.v + rbase + 16 * (s ^ swz(rr)))));
-      const uint32_t w0 = raw[0] & vmask[0], w1 = raw[1] & vmask[1];
-      u32x4 hv;
-      if constexpr (I8) {
-        const uint32_t x0 = w0 ^ 0x80808080u, x1 = w1 ^ 0x80808080u;
-        hv = (u32x4){widen_lo(x0), widen_hi(x0), widen_lo(x1), widen_hi(x1)};
+      frag_t va;
+      if constexpr (BF) {
+        // rows 8grp + 4h + (lane%16)/4, elements 16s + 4(lane%4) .. +3: lane gets 4 tokens of d
+        u32x4 w;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int rr = 8 * grp + 4 * h + ((lane & 15) >> 2);
+          const int chk = (2 * s + ((lane & 3) >> 1)) ^ swz(rr);
+          const i16x4 t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(L.v + rr * ROWB + 16 * chk + 8 * (lane & 1)));
+          const u32x2 t2 = __builtin_bit_cast(u32x2, t4);
+          w[2 * h] = t2[0] & vmask[2 * h];
+          w[2 * h + 1] = t2[1] & vmask[2 * h + 1];
+        }
+        va = __builtin_bit_cast(bf16x8, w);
       } else {
-        hv = (u32x4){fp8x2_lo(w0), fp8x2_hi(w0), fp8x2_lo(w1), fp8x2_hi(w1)};
+        const int rr = 8 * grp + ((lane & 15) >> 1);  // the row this lane addresses
+        const u32x2 raw = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                       (lds_v2i32*)(L.v + rr * ROWB + 16 * (s ^ swz(rr)) + 8 * (lane & 1))));
+        const uint32_t w0 = raw[0] & vmask[0], w1 = raw[1] & vmask[1];
+        u32x4 hv;
+        if constexpr (I8) {
+          const uint32_t x0 = w0 ^ 0x80808080u, x1 = w1 ^ 0x80808080u;
+          hv = (u32x4){widen_lo(x0), widen_hi(x0), widen_lo(x1), widen_hi(x1)};
+        } else {
+          hv = (u32x4){fp8x2_lo(w0), fp8x2_hi(w0), fp8x2_lo(w1), fp8x2_hi(w1)};
+        }
+        va = __builtin_bit_cast(f16x8, hv);
       }
-      o[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, hv), pf, o[s], 0, 0, 0);
+      if constexpr (BF)
+        o[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf, o[s], 0, 0, 0);
+      else
+        o[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pf, o[s], 0, 0, 0);
     }
   }
 
@@ -691,8 +749,10 @@ struct DecodeWaveM {
   }
 };
 
+// bf16 caches with few columns stream best with PV on the VALU (measured); byte caches and
+// 8 or more columns use the MFMA form
 template <int D, int GP, int KV>
-using DecodeWaveT = typename std::conditional<KV == kKvBf16, DecodeWave<D, GP, KV>,
+using DecodeWaveT = typename std::conditional<KV == kKvBf16 && GP < 8, DecodeWave<D, GP, KV>,
                                               DecodeWaveM<D, GP, KV>>::type;
 
 // ---- fixed split: one workgroup of 4 waves per (split, g, b) --------------------------------
@@ -707,8 +767,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     int n_split) {
   using W = DecodeWaveT<D, GP, KV>;
   constexpr int BS = W::BS, U = W::U;
-  __shared__ typename W::Lds s_lds[kDecodeWaves];
-  __shared__ float s_red[kDecodeWaves][GP][D];
+  // the V staging slices are dead once every wave has left its loop, and the per-wave O
+  // partials reuse their space (a barrier separates the two)
+  __shared__ union {
+    typename W::Lds lds[kDecodeWaves];
+    float red[kDecodeWaves][GP][D];
+  } s_u;
   __shared__ float s_ml[kDecodeWaves][2][GP];
   __shared__ int s_pb[kMaxSplitBlocks];  // the split's slice of the block table
 
@@ -763,11 +827,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
       c.pb[u] = c.okb[u] ? e : 0;
     }
     c.t0 = t_begin + blk0 * BS;
-    w.load(c, k_cache, v_cache, k_scale, v_scale, Hkv, g, s_lds[wave]);
+    w.load(c, k_cache, v_cache, k_scale, v_scale, Hkv, g, s_u.lds[wave]);
   };
   for (int ch = wave; ch < nchunk; ch += kDecodeWaves) {
     prep(cA, ch);
-    w.compute(cA, lo, t_end, scale_log2, s_lds[wave]);
+    w.compute(cA, lo, t_end, scale_log2, s_u.lds[wave]);
   }
 
   float l_w, ps_w;
@@ -776,10 +840,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     s_ml[wave][0][w.hq] = w.m_run;
     s_ml[wave][1][w.hq] = l_w;
   }
+  __syncthreads();  // every wave is done with the staging slices
   w.emit([&](int h, int d0, const auto& v) {
     constexpr int N = sizeof(v) / sizeof(v[0]);
 #pragma unroll
-    for (int e = 0; e < N; ++e) s_red[wave][h][d0 + e] = v[e];
+    for (int e = 0; e < N; ++e) s_u.red[wave][h][d0 + e] = v[e];
   });
   __syncthreads();
 
@@ -793,7 +858,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
 #pragma unroll
     for (int wv = 0; wv < kDecodeWaves; ++wv) {
       const float wt = fast_exp2(s_ml[wv][0][h] - M);  // waves that saw no token: l = 0, acc = 0
-      num = fmaf(wt, s_red[wv][h][d], num);
+      num = fmaf(wt, s_u.red[wv][h][d], num);
       den = fmaf(wt, s_ml[wv][1][h], den);
     }
     const float inv = den > 0.f ? 1.0f / den : 0.f;
