@@ -422,7 +422,7 @@ def main(argv=None):
     a_ms = avg_ms("a0", "a1")
     dbytes = decode_bytes(dwl, Dd["ctx_np"])
     d_gbs = dbytes / (d_ms * 1e-3) / 1e9
-    decode = {"kernel": "attn_decode_paged (split + merge)", "ms": d_ms, "GB/s": d_gbs,
+    decode = {"kernel": "attn_decode_paged (KV split across waves + log-sum-exp merge)", "ms": d_ms, "GB/s": d_gbs,
               "frac_hbm_peak": d_gbs / HBM_PEAK_GBS, "algorithmic_bytes": dbytes,
               "tokens_per_s": dwl.B / (d_ms * 1e-3), "append_ms": a_ms,
               "workload": f"{dwl.name}: B={dwl.B} Hq={dwl.Hq} Hkv={dwl.Hkv} D={dwl.D} kv={dwl.kv_dtype} "
