@@ -18,6 +18,12 @@ kv_cache_append_rope (a 64k-token prompt written into a paged cache with RoPE on
 attn_decode_paged over an FP8 E4M3 copy of the decode cache. `--workload fp8_70b` runs the
 INT8 70B-shaped decode with an FP8 cache instead.
 
+Before touching the GPU, bench.py runs attention_attn_prefill_amd/attn_peaks (built with the
+library) as a child process: a bf16 MFMA-only loop (with the shader clock it ran at), an HBM
+streaming read and a random 2 KB-block gather; the JSON line carries them as
+`measured_peaks`, and each roofline object adds `frac_of_measured` beside the fraction of the
+published peak. Per-call times also come as p10 / p50 / p90 over the timed steps.
+
 Prints one JSON line. Inputs are seeded synthetic tensors (synth/) resident in HBM before the
 timed region starts.
 """
@@ -338,6 +344,22 @@ def cpu_baseline(pwl, dwl, budget_s: float):
                       f"{pwl.name}, all {pwl.S} rows each, {el:.1f} s; BLAS threads = cores"}
 
 
+def measured_peaks() -> dict | None:
+    """Run the measured-ceiling program built next to the library (bf16 MFMA loop, shader
+    clock, HBM streaming read, random 2 KB gather) as a child process; None if not built."""
+    import subprocess
+    exe = os.path.join(ROOT, "attention_attn_prefill_amd", "attn_peaks")
+    if not os.path.exists(exe):
+        return None
+    try:
+        r = subprocess.run([exe], capture_output=True, text=True, timeout=180)
+    except subprocess.TimeoutExpired:
+        return {"error": "timed out"}
+    if r.returncode != 0:
+        return {"error": r.stderr.strip()[-300:]}
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -348,6 +370,8 @@ def main(argv=None):
     ap.add_argument("--no-flush", action="store_true", help="skip the cache-evicting scratch read")
     ap.add_argument("--no-chunked", action="store_true",
                     help="skip the chunked-prefill and multi-row-decode timings reported beside the step")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured-ceiling program (MFMA loop, HBM read and gather)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 3 times (counter calibration)")
     args = ap.parse_args(argv)
@@ -355,6 +379,9 @@ def main(argv=None):
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the attention "
               "path in this repository runs on a single GPU", file=sys.stderr)
         return 2
+
+    # measured ceilings first, in a child process, before this process touches the GPU
+    peaks = None if (args.no_peaks or args.copy_calibration) else measured_peaks()
 
     import torch as t
     import attention_attn_prefill_amd as A
@@ -418,13 +445,18 @@ def main(argv=None):
     def avg_ms(a, b):
         return float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
 
+    def pct_ms(a, b):  # p10 / p50 / p90 of one call over the timed steps
+        x = np.array([e[a].elapsed_time(e[b]) for e in evs])
+        return {"p10": float(np.percentile(x, 10)), "p50": float(np.percentile(x, 50)),
+                "p90": float(np.percentile(x, 90))}
+
     d_ms = avg_ms("d0", "d1")
     a_ms = avg_ms("a0", "a1")
     dbytes = decode_bytes(dwl, Dd["ctx_np"])
     d_gbs = dbytes / (d_ms * 1e-3) / 1e9
     decode = {"kernel": "attn_decode_paged (KV split across waves + log-sum-exp merge)", "ms": d_ms, "GB/s": d_gbs,
               "frac_hbm_peak": d_gbs / HBM_PEAK_GBS, "algorithmic_bytes": dbytes,
-              "tokens_per_s": dwl.B / (d_ms * 1e-3), "append_ms": a_ms,
+              "tokens_per_s": dwl.B / (d_ms * 1e-3), "append_ms": a_ms, "ms_percentiles": pct_ms("d0", "d1"),
               "workload": f"{dwl.name}: B={dwl.B} Hq={dwl.Hq} Hkv={dwl.Hkv} D={dwl.D} kv={dwl.kv_dtype} "
                           f"ctx=[{dwl.ctx_lo},{dwl.ctx_hi}] window={dwl.window} block=16"}
     roofline_decode = {"bound": "hbm", "achieved": d_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -443,6 +475,7 @@ def main(argv=None):
                            "frac": p_tf / BF16_PEAK_TFLOPS,
                            "traffic": measured_traffic("prefill", pwl.name)}
         out["prefill"] = {"kernel": "attn_prefill (bf16 MFMA)", "ms": p_ms, "TFLOP/s": p_tf,
+                          "ms_percentiles": pct_ms("p0", "p1"),
                           "algorithmic_flops": pfl, "tokens_per_s": pwl.B * pwl.S / (p_ms * 1e-3),
                           "workload": f"{pwl.name}: B={pwl.B} S={pwl.S} Hq={pwl.Hq} Hkv={pwl.Hkv} "
                                       f"D={pwl.D} causal window={pwl.window}"}
@@ -451,6 +484,15 @@ def main(argv=None):
         out["roofline"] = roofline_decode
     out["decode"] = decode
     out["roofline_decode"] = roofline_decode
+    if peaks is not None:
+        # the same achieved figures against ceilings measured on this device: the bf16 MFMA
+        # loop for prefill, the random 2 KB-block gather (the paged cache's access pattern) for
+        # decode
+        out["measured_peaks"] = peaks
+        if "mfma_bf16_tflops" in peaks and "roofline" in out and out["roofline"]["bound"] == "mfma":
+            out["roofline"]["frac_of_measured"] = out["roofline"]["achieved"] / peaks["mfma_bf16_tflops"]
+        if "hbm_gather_2k_gbs" in peaks:
+            roofline_decode["frac_of_measured"] = d_gbs / peaks["hbm_gather_2k_gbs"]
     out["config"] = {"workload": (f"{pwl.name} + {dwl.name}" if pwl else dwl.name),
                      "step": "kv_cache_append -> cache flush -> attn_decode_paged -> attn_prefill"}
     if args.workload == "llama1b" and not args.no_chunked:
