@@ -47,6 +47,12 @@ __device__ __forceinline__ void lds_dma_16(const void* g, uint32_t lds_off) {
                : "memory", "m0");
 }
 
+// As lds_dma_16 with one dword per lane: LDS byte address lds_off + 4 * lane.
+__device__ __forceinline__ void lds_dma_4(const void* g, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_off), "v"(g)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const lds_void*)p;
 }

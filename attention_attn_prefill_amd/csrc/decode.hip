@@ -951,38 +951,41 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
     const int32_t* __restrict__ ctx_lens, uint16_t* __restrict__ out,
     int32_t* __restrict__ prefix_out, float* __restrict__ part_o, float* __restrict__ part_lse,
     int B, int Hq, int Hkv, int G, int QL, int max_blocks, int num_blocks, int max_ctx,
-    float scale_log2, int window) {
+    float scale_log2) {
   using W = DecodeWaveT<D, GP, KV>;
   constexpr int BS = W::BS, U = W::U;
-  constexpr int NSLOT = W::kMfmaPv ? 2 : 1;  // byte caches: the next chunk's V lands in slot 1
+  constexpr int NSLOT = W::kMfmaPv ? 2 : 1;  // MFMA form: the next chunk's V lands in slot 1
   __shared__ typename W::Lds s_lds[kDecodeWaves][NSLOT];
   __shared__ int s_pre[kStreamMaxB + 1];
-  __shared__ int s_scan[kDecodeThreads];
+  __shared__ int s_wsum[kDecodeWaves];
+  __shared__ int s_tab[kDecodeWaves][2][64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // ---- prefix of visible blocks over the sequences (every workgroup; workgroup 0 also
-  // stores it for the merge) --------------------------------------------------------------
+  // stores it for the merge): per-thread runs, a scan inside each wave, then the wave totals
   {
     const int per = (B + kDecodeThreads - 1) / kDecodeThreads;
     const int b0 = tid * per;
     int run = 0;
     for (int i = 0; i < per && b0 + i < B; ++i)
-      run += visible_blocks(ctx_lens, b0 + i, max_ctx, max_blocks, window, QL);
-    s_scan[tid] = run;
-    __syncthreads();
-    for (int o = 1; o < kDecodeThreads; o <<= 1) {  // inclusive scan
-      const int add = tid >= o ? s_scan[tid - o] : 0;
-      __syncthreads();
-      s_scan[tid] += add;
-      __syncthreads();
+      run += visible_blocks(ctx_lens, b0 + i, max_ctx, max_blocks, 0, QL);
+    int incl = run;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
     }
-    run = tid > 0 ? s_scan[tid - 1] : 0;
+    if (lane == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int w2 = 0; w2 < wave; ++w2) base += s_wsum[w2];
+    run = base + incl - run;  // exclusive prefix of this thread's first sequence
     for (int i = 0; i < per && b0 + i < B; ++i) {
       s_pre[b0 + i] = run;
-      run += visible_blocks(ctx_lens, b0 + i, max_ctx, max_blocks, window, QL);
+      run += visible_blocks(ctx_lens, b0 + i, max_ctx, max_blocks, 0, QL);
     }
-    if (tid == kDecodeThreads - 1) s_pre[B] = s_scan[tid];
+    if (tid == kDecodeThreads - 1) s_pre[B] = base + incl;
     __syncthreads();
     if (blockIdx.x == 0)
       for (int i = tid; i <= B; i += kDecodeThreads) prefix_out[i] = s_pre[i];
@@ -992,83 +995,132 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
   const int P = gridDim.x * kDecodeWaves;
   const int64_t qn = (T + P - 1) / P;
   const int p = blockIdx.x * kDecodeWaves + wave;
-  int64_t pos = p * qn;
-  const int64_t end = min(pos + qn, T);
-  if (pos >= end) return;  // no barrier follows
+  const int64_t pos0 = p * qn;
+  const int64_t end = min(pos0 + qn, T);
+  if (pos0 >= end) return;  // no barrier follows
 
-  // the segment holding entry pos: the last b with Hkv * pre[b] <= pos (it has nvis(b) > 0)
+  // the segment holding entry pos0: the last b with Hkv * pre[b] <= pos0 (it has nvis(b) > 0)
   int b = 0;
   {
     int lo_b = 0, hi_b = B - 1;
     while (lo_b < hi_b) {
       const int mid = (lo_b + hi_b + 1) >> 1;
-      if ((int64_t)Hkv * s_pre[mid] <= pos) lo_b = mid; else hi_b = mid - 1;
+      if ((int64_t)Hkv * s_pre[mid] <= pos0) lo_b = mid; else hi_b = mid - 1;
     }
     b = lo_b;
   }
   int nv = s_pre[b + 1] - s_pre[b];
-  int g = (int)((pos - (int64_t)Hkv * s_pre[b]) / nv);
+  int g = (int)((pos0 - (int64_t)Hkv * s_pre[b]) / nv);
+
+  // Table entries of the wave's list range, 64 at a time: lane i of window k holds the entry
+  // of list position pos0 + 64k + i. Windows are copied global -> LDS (two per wave) and the
+  // next one is in flight while the current one is used, so neither a 64-entry boundary nor a
+  // segment boundary waits on a table load; the copy is awaited only when a window begins
+  // (a register copy of an in-flight load would make every later use wait for all loads).
+  // The segment of each lane's position is found in the prefix (at or after sequence b_hint).
+  auto fetch_window = [&](int64_t w0, int b_hint, int buf) {
+    const int64_t e = w0 + lane;
+    const int32_t* src = table;  // lanes past the range copy any valid entry, never used
+    if (e < end) {
+      int lo_b = b_hint, hi_b = B - 1;
+      while (lo_b < hi_b) {
+        const int mid = (lo_b + hi_b + 1) >> 1;
+        if ((int64_t)Hkv * s_pre[mid] <= e) lo_b = mid; else hi_b = mid - 1;
+      }
+      const int nvb = s_pre[lo_b + 1] - s_pre[lo_b];
+      const int r = (int)(e - (int64_t)Hkv * s_pre[lo_b]);  // g * nvb + block
+      src = table + (int64_t)lo_b * max_blocks + r % nvb;   // no window: block 0 is visible
+    }
+    lds_dma_4(src, lds_addr(&s_tab[wave][buf][0]));
+  };
+  int64_t wbase = pos0;
+  int wk = 0;
+  fetch_window(pos0, b, 0);
+  if (pos0 + 64 < end) fetch_window(pos0 + 64, b, 1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  int tab = s_tab[wave][0][lane];
+  auto entry = [&](int64_t e) -> int {  // e: list position, visited in increasing order
+    if (e - wbase >= 64) {
+      wbase += 64;
+      ++wk;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // window wk has landed
+      tab = s_tab[wave][wk & 1][lane];
+      if (wbase + 64 < end) fetch_window(wbase + 64, b, (wk + 1) & 1);
+    }
+    return __builtin_amdgcn_readlane(tab, (int)(e - wbase));
+  };
+
+  // current piece: list positions [pos, pend) of segment (b, g), blocks j0 .. j1-1
+  int64_t seg0 = (int64_t)Hkv * s_pre[b] + (int64_t)g * nv;
+  int64_t pend = min(end, seg0 + nv);
+  int j0 = (int)(pos0 - seg0), j1 = (int)(pend - seg0);
+  int ctx = decode_ctx(ctx_lens, b, max_ctx, max_blocks, BS);
+  int hi = min(j1 * BS, ctx);
 
   W w;
   w.init(lane);
-  while (true) {
-    const int64_t seg0 = (int64_t)Hkv * s_pre[b] + (int64_t)g * nv;
-    const int64_t pend = min(end, seg0 + nv);
-    const int j0 = (int)(pos - seg0), j1 = (int)(pend - seg0);
-    const int ctx = decode_ctx(ctx_lens, b, max_ctx, max_blocks, BS);
-    const int lo = first_key(ctx, QL, window);
-    const int lb0 = lo / BS;  // first visible block
-    const int32_t* trow = table + (int64_t)b * max_blocks + lb0;
-
-    const int hi = min((lb0 + j1) * BS, ctx);
-    // the piece's table entries, 64 at a time: lane i holds entry win + i
-    int win = j0;
-    int tab = j0 + lane < j1 ? trow[j0 + lane] : -1;
-    typename W::Chunk cA;
-    auto prep = [&](typename W::Chunk& c, int j, int slot) {
+  typename W::Chunk cA;
+  auto prep = [&](typename W::Chunk& c, int j, int slot) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        int e = -1;
-        if (j + u < j1) {
-          if (j + u - win >= 64) {
-            win += 64;
-            tab = win + lane < j1 ? trow[win + lane] : -1;
-          }
-          e = __builtin_amdgcn_readlane(tab, j + u - win);
-        }
-        c.okb[u] = e >= 0 && e < num_blocks;  // unusable entry: its tokens are skipped
-        c.pb[u] = c.okb[u] ? e : 0;
-      }
-      c.t0 = (lb0 + j) * BS;
-      w.load(c, k_cache, v_cache, k_scale, v_scale, Hkv, g, s_lds[wave][slot]);
-    };
+    for (int u = 0; u < U; ++u) {
+      const int e = j + u < j1 ? entry(seg0 + j + u) : -1;
+      c.okb[u] = e >= 0 && e < num_blocks;  // unusable entry: its tokens are skipped
+      c.pb[u] = c.okb[u] ? e : 0;
+    }
+    c.t0 = j * BS;
+    w.load(c, k_cache, v_cache, k_scale, v_scale, Hkv, g, s_lds[wave][slot]);
+  };
 
-    w.load_q(q, b, g, G, QL, Hq, ctx, window);
-    w.reset();
+  w.load_q(q, b, g, G, QL, Hq, ctx, 0);
+  w.reset();
+  prep(cA, j0, 0);
+  const int ncol = G * QL;
+  while (true) {
+    // ---- the chunks of the piece; cA holds the first one's loads --------------------------
     if constexpr (W::kMfmaPv) {
       // two chunks in flight: the next chunk's loads are issued before this one is computed
       typename W::Chunk cB;
-      if (j0 < j1) prep(cA, j0, 0);
-      for (int j = j0; j < j1; j += 2 * U) {
+      for (int j = j0;; j += 2 * U) {
         const bool nb = j + U < j1;
         if (nb) prep(cB, j + U, 1);
-        w.compute(cA, lo, hi, scale_log2, s_lds[wave][0], nb);
+        w.compute(cA, 0, hi, scale_log2, s_lds[wave][0], nb);
         if (!nb) break;
         const bool na = j + 2 * U < j1;
         if (na) prep(cA, j + 2 * U, 0);
-        w.compute(cB, lo, hi, scale_log2, s_lds[wave][1], na);
+        w.compute(cB, 0, hi, scale_log2, s_lds[wave][1], na);
+        if (!na) break;
       }
     } else {
-      for (int j = j0; j < j1; j += U) {
-        prep(cA, j, 0);
-        w.compute(cA, lo, hi, scale_log2, s_lds[wave][0]);
+      for (int j = j0;; j += U) {
+        if (j > j0) prep(cA, j, 0);
+        w.compute(cA, 0, hi, scale_log2, s_lds[wave][0]);
+        if (j + U >= j1) break;
       }
     }
+
+    // ---- the next piece's Q and first chunk are issued before this one is written out -----
+    const int ob = b, og = g;
+    const bool whole = j0 == 0 && j1 == nv;
+    const bool more = pend < end;
+    if (more) {
+      if (++g == Hkv) {  // next sequence with visible blocks (one exists: pend < T)
+        g = 0;
+        do ++b; while (s_pre[b + 1] == s_pre[b]);
+        nv = s_pre[b + 1] - s_pre[b];
+        ctx = decode_ctx(ctx_lens, b, max_ctx, max_blocks, BS);
+      }
+      seg0 = pend;
+      pend = min(end, seg0 + nv);
+      j0 = 0;
+      j1 = (int)(pend - seg0);
+      hi = min(j1 * BS, ctx);
+      w.load_q(q, b, g, G, QL, Hq, ctx, 0);
+      prep(cA, 0, 0);
+    }
+
     float l_w, ps_w;
     w.reduce(l_w, ps_w);
-    const bool whole = j0 == 0 && j1 == nv;
-    const int64_t slot = (int64_t)b * Hkv + g + p;
-    const int ncol = G * QL;
+    const int64_t slot = (int64_t)ob * Hkv + og + p;
     // column h's row sum and max: lane h holds them (both lane layouts)
     float lcol[GP], mcol[GP];
 #pragma unroll
@@ -1093,7 +1145,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
         uint32_t o2[N / 2];
 #pragma unroll
         for (int e = 0; e < N / 2; ++e) o2[e] = pack_bf16x2(v[2 * e] * inv, v[2 * e + 1] * inv);
-        const int64_t orow = ((int64_t)b * QL + h / G) * Hq + g * G + h % G;
+        const int64_t orow = ((int64_t)ob * QL + h / G) * Hq + og * G + h % G;
         uint16_t* dst = out + orow * D + d0;
         if constexpr (N == 8)
           *reinterpret_cast<u32x4*>(dst) = (u32x4){o2[0], o2[1], o2[2], o2[3]};
@@ -1107,13 +1159,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
         if (d0 == 0) part_lse[slot * ncol + h] = lh > 0.f ? mh + __log2f(lh) : -INFINITY;
       }
     });
-    pos = pend;
-    if (pos >= end) break;
-    if (++g == Hkv) {  // next sequence with visible blocks (one exists: pos < T)
-      g = 0;
-      do ++b; while (s_pre[b + 1] == s_pre[b]);
-      nv = s_pre[b + 1] - s_pre[b];
-    }
+    if (!more) break;
+    w.reset();
   }
 }
 
@@ -1226,7 +1273,7 @@ static void launch_stream(const DecodeArgs& a, hipStream_t stream) {
                      a.k_cache, a.v_cache, (const __half*)a.k_scale, (const __half*)a.v_scale,
                      a.block_table, a.context_lens, (uint16_t*)a.o, prefix, part_o, part_lse, a.B,
                      a.Hq, a.Hkv, G, a.q_len, a.max_blocks_per_seq, a.num_blocks,
-                     a.max_context_len, a.scale * kLog2e, a.window);
+                     a.max_context_len, a.scale * kLog2e);
   hipLaunchKernelGGL(decode_stream_merge_kernel<D>, dim3(a.Hkv * G * a.q_len, a.B), dim3(64), 0,
                      stream, prefix, part_o, part_lse, (uint16_t*)a.o, a.B, a.Hq, a.Hkv, G,
                      a.q_len, wgs * kDecodeWaves);
