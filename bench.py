@@ -24,6 +24,9 @@ streaming read and a random 2 KB-block gather; the JSON line carries them as
 `measured_peaks`, and each roofline object adds `frac_of_measured` beside the fraction of the
 published peak. Per-call times also come as p10 / p50 / p90 over the timed steps.
 
+The cpu_baseline leg times the fp64 oracle on (batch, head) pairs of the same prefill, and
+compares them with the timed run's output (`prefill.max_abs_err_vs_oracle`, untimed).
+
 Prints one JSON line. Inputs are seeded synthetic tensors (synth/) resident in HBM before the
 timed region starts.
 """
@@ -318,30 +321,42 @@ def time_decode_fp8(t, A, dwl, Dd, reps: int):
             "workload": f"{dwl.name} shapes with the cache quantized to FP8 E4M3 + fp16 per-token scales"}
 
 
-def cpu_baseline(pwl, dwl, budget_s: float):
-    """The oracle, untuned, on a time-bounded sample of the same workload."""
+def cpu_baseline(pwl, dwl, budget_s: float, o_gpu=None):
+    """The oracle, untuned, on a time-bounded sample of the same workload. With o_gpu (the
+    timed prefill's output on the host, [B][S][Hq][D] float64) it also reports the largest
+    |GPU - oracle| over the sampled (batch, head) pairs; the comparison is not timed."""
     import oracle
     from synth import prefill_slab
+    cores, blas = 1, "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            cores = max(i.get("num_threads", 1) for i in libs)
+            blas = ",".join(sorted({str(i.get("internal_api")) for i in libs}))
     except Exception:  # pragma: no cover
-        cores = 1
+        pass
     G = pwl.Hq // pwl.Hkv
     pos = np.arange(pwl.S)
-    heads, flops, t0 = 0, 0.0, time.perf_counter()
-    while heads < pwl.Hq * pwl.B and time.perf_counter() - t0 < budget_s:
+    heads, flops, el, err = 0, 0.0, 0.0, 0.0
+    while heads < pwl.Hq * pwl.B and el < budget_s:
         b, h = divmod(heads, pwl.Hq)
         q = prefill_slab(pwl, "q", b, h)
         k = prefill_slab(pwl, "k", b, h // G)
         v = prefill_slab(pwl, "v", b, h // G)
-        oracle.attention_head(q, k, v, pwl.scale, pos, pwl.causal, pwl.window)
+        t0 = time.perf_counter()
+        ro, _ = oracle.attention_head(q, k, v, pwl.scale, pos, pwl.causal, pwl.window)
+        el += time.perf_counter() - t0
+        if o_gpu is not None:
+            err = max(err, float(np.max(np.abs(o_gpu[b, :, h, :] - ro))))
         heads += 1
         flops += 4.0 * pwl.D * prefill_pairs(pwl.S, pwl.causal, pwl.window)
-    el = time.perf_counter() - t0
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"fp64 NumPy oracle prefill of {heads} of {pwl.Hq * pwl.B} (batch, head) pairs of "
-                      f"{pwl.name}, all {pwl.S} rows each, {el:.1f} s; BLAS threads = cores"}
+    out = {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+           "sample": f"fp64 NumPy oracle prefill of {heads} of {pwl.Hq * pwl.B} (batch, head) pairs of "
+                     f"{pwl.name}, all {pwl.S} rows each, {el:.1f} s; BLAS ({blas}) threads = cores"}
+    if o_gpu is not None:
+        out["prefill_max_abs_err"] = err  # the timed run's output, bf16, against the fp64 oracle
+    return out
 
 
 def measured_peaks() -> dict | None:
@@ -363,8 +378,8 @@ def measured_peaks() -> dict | None:
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama1b", choices=["llama1b", "swa", "int8_70b", "fp8_70b"])
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0 = skip)")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache-evicting scratch read")
@@ -501,7 +516,9 @@ def main(argv=None):
         out["append_rope"] = time_append_rope(t, A, max(5, args.steps))
         out["decode_fp8"] = time_decode_fp8(t, A, dwl, Dd, max(5, args.steps))
     if args.cpu_budget > 0 and pwl is not None:
-        out["cpu_baseline"] = cpu_baseline(pwl, dwl, args.cpu_budget)
+        o_host = P["o"].float().cpu().numpy().astype(np.float64)
+        out["cpu_baseline"] = cpu_baseline(pwl, dwl, args.cpu_budget, o_host)
+        out["prefill"]["max_abs_err_vs_oracle"] = out["cpu_baseline"]["prefill_max_abs_err"]
     print(json.dumps(out), flush=True)
     return 0
 
