@@ -349,6 +349,20 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(
     if (j < jhi) issue_tile(j + 1, st ^ 1);
 
     const int k0 = j * kBN;
+    if constexpr (PAGED) {
+      // Keys no row of the workgroup can see (past the context, left of the window) come
+      // from unwritten slots, blocks left of the window or stand-in blocks and may hold
+      // anything: their scores are masked, but 0 * NaN in the PV contraction would still be
+      // NaN, so their V rows are zeroed (whole rows: the swizzle only permutes chunks).
+      if (k0 < kmin || k0 + kBN > Lk) {
+        char* vt = smem + st * T::STAGE + T::TILE;
+        for (int i = tid; i < kBN * T::CHUNKS; i += kPrefillThreads) {
+          const int key = k0 + i / T::CHUNKS;
+          if (key < kmin || key >= Lk) *reinterpret_cast<u32x4*>(vt + 16 * i) = (u32x4){0u, 0u, 0u, 0u};
+        }
+        __syncthreads();
+      }
+    }
     // A tile outside this wave's key range (other waves of the workgroup need it) runs
     // masked: every score is -inf, so it adds nothing and triggers no rescale.
     const bool relevant = wave_live && k0 <= kmax_w && k0 + kBN - 1 >= kmin_w;

@@ -101,7 +101,10 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, float* ls
  *  max_q_len    : host-side bound on every q_len_b, used to size the grid.
  *  Requirements: D in {64, 128}; block_size == 16; Hq % Hkv == 0; total_q >= 0 (0 is a no-op);
  *  causal and window as in attn_prefill; bf16 only. Rows whose chunk is longer than the context
- *  are left unwritten; table entries outside [0, num_blocks) are never dereferenced.
+ *  are left unwritten; table entries outside [0, num_blocks) are never dereferenced. Cache
+ *  slots that hold no key visible to any row of the chunk (past the context, or left of every
+ *  row's window) may hold anything, NaN included, and the table entries of blocks made only
+ *  of such slots may hold anything: that content never reaches the result.
  */
 int attn_prefill_paged(const void* q, const void* k_new, const void* v_new, void* k_cache,
                        void* v_cache, const int32_t* block_table, const int32_t* cu_q,

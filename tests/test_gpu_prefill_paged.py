@@ -127,3 +127,40 @@ def test_prefill_paged_llama1b_chunk_sampled():
         for h in (0, 5, 31):
             ro, _ = oracle.attention_head(q[:, h], kk[:, h // 4], vv[:, h // 4], c["scale"], 3072 + rows, True, 0)
             assert maxabs(got[sel, h], ro) <= BF16_TOL
+
+
+def _poison(c, window):
+    """Copy of case c whose invisible cache content is NaN: slots past each context, spare
+    blocks, and blocks wholly left of the window of every row of the chunk; the table entries
+    of blocks no row can see (past the context, left of the window) become -1."""
+    nan = np.uint16(0x7FC0)
+    p = dict(c)
+    kb, vb, table = c["kb"].copy(), c["vb"].copy(), c["table"].copy()
+    live = np.zeros(kb.shape[0] * 16, bool)
+    for b, (ctx, n) in enumerate(zip(c["ctx"], c["q_len"])):
+        first = max(0, int(ctx) - int(n) - window + 1) if window > 0 and n > 0 else 0
+        for t in range(first - first % 16, int(ctx)):  # blocks holding a visible key
+            live[int(table[b][t // 16]) * 16 + t % 16] = t >= first
+        table[b, : first // 16] = -1
+        table[b, -(-int(ctx) // 16):] = -1
+    for s in np.nonzero(~live)[0]:
+        kb[s // 16, :, s % 16] = nan
+        vb[s // 16, :, s % 16] = nan
+    p.update(kb=kb, vb=vb, table=table)
+    return p
+
+
+@pytest.mark.parametrize("ctx,q_len,Hq,Hkv,D,window", [
+    ((300, 17, 1000, 70), (300, 1, 130, 6), 8, 2, 64, 0),
+    ((2000, 129, 77), (700, 129, 5), 8, 2, 128, 300),
+])
+def test_prefill_paged_ignores_invisible_cache_content(ctx, q_len, Hq, Hkv, D, window):
+    """NaN in every cache slot no row can see, and -1 table entries for the blocks no row can
+    see, leave the output unchanged (0 * NaN must never reach the PV contraction)."""
+    c = _case(ctx, q_len, Hq, Hkv, D, seed=650 + D + window)
+    ro, rl, _, _ = _expected(c, window)
+    o, L, _, _ = _run(_poison(c, window), window)
+    got = host_f64(o)
+    assert np.isfinite(got).all()
+    assert maxabs(got, ro) <= BF16_TOL
+    assert maxabs(host_f64(L), rl) <= LSE_TOL_BF16
