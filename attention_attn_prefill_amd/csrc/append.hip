@@ -13,7 +13,7 @@
 // "3.1 RMSNorm + RoPE 融合" on the triton-fused-ops page ("Triton融合算子优化：LLM推理性能提升3倍
 // 的工程实践"). The pages give no formula; this library takes the Llama convention: dimension
 // i < D/2 pairs with i + D/2 and the pair turns by pos * base^(-2i/D). The frequencies come
-// from an fp64 table built once per workgroup; the angle and its reduction modulo 2*pi are
+// from an fp64 table built once per call on the host; the angle and its reduction modulo 2*pi are
 // fp64 (positions reach tens of thousands of radians); sin, cos and the rotation are fp32,
 // rounded to bf16 (RNE) when stored as bf16. Each (token, pair) angle is evaluated once per
 // workgroup and shared by the token's heads through LDS.
@@ -25,15 +25,15 @@
 #include "common.h"
 #include "launch.h"
 #include <hip/hip_fp16.h>
+#include <cmath>
 
 namespace attn {
 
-// inv_freq[i] = base^(-2i/D), i < D/2, in LDS
-template <int D>
-__device__ __forceinline__ void rope_table(double* inv_freq, double base) {
-  for (int i = threadIdx.x; i < D / 2; i += blockDim.x) inv_freq[i] = pow(base, -2.0 * i / D);
-  __syncthreads();
-}
+// inv_freq[i] = base^(-2i/D), i < D/2: computed once on the host (fp64 pow) and passed by
+// value, so no workgroup evaluates pow or waits for a table of its own.
+struct RopeFreq {
+  double f[64];
+};
 
 // The angle of a pair depends only on (position, pair index), so a workgroup computes each
 // (token, pair) of its rows once: the first of its rows that belongs to a token fills that
@@ -41,13 +41,13 @@ __device__ __forceinline__ void rope_table(double* inv_freq, double base) {
 // token reads it after a barrier. Same arithmetic for every element as computing it in place.
 template <int D>
 __device__ __forceinline__ void rope_fill(float2* __restrict__ row_cs, int c, int pos,
-                                          const double* inv_freq) {
+                                          const RopeFreq& rf) {
   constexpr int TPR = D / 8;
   constexpr double kTwoPi = 6.283185307179586476925286766559;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int i = c + TPR * k;
-    const double ang = (double)pos * inv_freq[i];
+    const double ang = (double)pos * rf.f[i];
     const float r = (float)(ang - kTwoPi * rint(ang * (1.0 / kTwoPi)));  // in [-pi, pi]
     float sn, cs;
     sincosf(r, &sn, &cs);
@@ -78,12 +78,10 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     const int32_t* __restrict__ table, void* __restrict__ k_cache, void* __restrict__ v_cache,
     __half* __restrict__ k_scale, __half* __restrict__ v_scale, int64_t rows, int Hkv, int bs,
     int num_seqs, int max_blocks, int num_blocks, const int32_t* __restrict__ cu_q,
-    const int32_t* __restrict__ ctx, double rope_base) {
+    const int32_t* __restrict__ ctx, RopeFreq rf) {
   constexpr int TPR = D / 8;        // threads per (token, head) row
   constexpr int ROWS = 256 / TPR;   // rows per workgroup
-  __shared__ double s_inv[ROPE ? D / 2 : 1];
   __shared__ float2 s_cs[ROPE ? ROWS : 1][ROPE ? D / 2 : 1];
-  if constexpr (ROPE) rope_table<D>(s_inv, rope_base);
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t row = gid / TPR;
   const int c = (int)(gid % TPR);
@@ -129,7 +127,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     const int64_t r0 = (int64_t)blockIdx.x * ROWS;
     const int64_t first = t * Hkv > r0 ? t * Hkv : r0;
     cs_row = (int)(first - r0);
-    if (in_range && r == first) rope_fill<D>(s_cs[cs_row], c, rpos, s_inv);
+    if (in_range && r == first) rope_fill<D>(s_cs[cs_row], c, rpos, rf);
     __syncthreads();
   }
 
@@ -199,12 +197,10 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
 template <int D>
 __global__ __launch_bounds__(256) void rope_rows_kernel(uint16_t* __restrict__ x,
                                                         const int32_t* __restrict__ pos,
-                                                        int64_t rows, int H, double rope_base) {
+                                                        int64_t rows, int H, RopeFreq rf) {
   constexpr int TPR = D / 8;
   constexpr int ROWS = 256 / TPR;
-  __shared__ double s_inv[D / 2];
   __shared__ float2 s_cs[ROWS][D / 2];
-  rope_table<D>(s_inv, rope_base);
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t row = gid / TPR;
   const int c = (int)(gid % TPR);
@@ -216,7 +212,7 @@ __global__ __launch_bounds__(256) void rope_rows_kernel(uint16_t* __restrict__ x
   const int64_t t = r / H, r0 = (int64_t)blockIdx.x * ROWS;
   const int64_t first = t * H > r0 ? t * H : r0;  // the token's first row in the workgroup
   const int cs_row = (int)(first - r0);
-  if (in_range && r == first) rope_fill<D>(s_cs[cs_row], c, pos[t], s_inv);
+  if (in_range && r == first) rope_fill<D>(s_cs[cs_row], c, pos[t], rf);
   __syncthreads();
   float v[8];
 #pragma unroll
@@ -230,9 +226,16 @@ __global__ __launch_bounds__(256) void rope_rows_kernel(uint16_t* __restrict__ x
   if (in_range) *reinterpret_cast<u32x4*>(p) = w;
 }
 
+static RopeFreq rope_freq(int D, double base) {
+  RopeFreq rf{};
+  for (int i = 0; i < D / 2 && i < 64; ++i) rf.f[i] = std::pow(base, -2.0 * i / D);
+  return rf;
+}
+
 template <bool VARLEN, bool ROPE>
 static int launch_append(const AppendArgs& a, const int32_t* cu_q, const int32_t* ctx,
                          double rope_base, hipStream_t stream) {
+  const RopeFreq rf = ROPE ? rope_freq(a.D, rope_base) : RopeFreq{};
   const int64_t rows = (int64_t)a.T * a.Hkv;
   const int tpr = a.D / 8;
   const int64_t threads = rows * tpr;
@@ -244,7 +247,7 @@ static int launch_append(const AppendArgs& a, const int32_t* cu_q, const int32_t
                      0, stream, (const uint16_t*)a.k_new, (const uint16_t*)a.v_new, a.seq_idx,  \
                      a.pos, a.block_table, a.k_cache, a.v_cache, (__half*)a.k_scale,            \
                      (__half*)a.v_scale, rows, a.Hkv, a.block_size, a.num_seqs,                 \
-                     a.max_blocks_per_seq, a.num_blocks, cu_q, ctx, rope_base)
+                     a.max_blocks_per_seq, a.num_blocks, cu_q, ctx, rf)
   if (a.D == 64) {
     if (a.kv == kKvI8) ATTN_APPEND(64, kKvI8); else if (a.kv == kKvFp8) ATTN_APPEND(64, kKvFp8); else ATTN_APPEND(64, kKvBf16);
   } else {
@@ -272,12 +275,13 @@ int launch_rope_rows(void* x, const int32_t* pos, int T, int H, int D, double ro
   const int64_t rows = (int64_t)T * H;
   const int64_t grid = (rows * (D / 8) + 255) / 256;
   if (grid == 0) return 0;
+  const RopeFreq rf = rope_freq(D, rope_base);
   if (D == 64)
     hipLaunchKernelGGL(rope_rows_kernel<64>, dim3((unsigned)grid), dim3(256), 0, stream,
-                       (uint16_t*)x, pos, rows, H, rope_base);
+                       (uint16_t*)x, pos, rows, H, rf);
   else
     hipLaunchKernelGGL(rope_rows_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream,
-                       (uint16_t*)x, pos, rows, H, rope_base);
+                       (uint16_t*)x, pos, rows, H, rf);
   return 0;
 }
 
