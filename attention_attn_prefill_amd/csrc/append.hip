@@ -36,23 +36,29 @@ struct RopeFreq {
 };
 
 // The angle of a pair depends only on (position, pair index), so a workgroup computes each
-// (token, pair) of its rows once: the first of its rows that belongs to a token fills that
-// token's (cos, sin) table in LDS, four pairs per lane (D/2 = 4 * TPR), and every row of the
-// token reads it after a barrier. Same arithmetic for every element as computing it in place.
+// (token, pair) of its rows once: the (cos, sin) table of the tokens its rows cover,
+// tokens t_a .. t_a + ntok - 1, one entry per thread (all threads take part), in LDS behind one
+// barrier; every row of a token reads the token's table. Same arithmetic for every element as
+// computing it in place.
 template <int D>
-__device__ __forceinline__ void rope_fill(float2* __restrict__ row_cs, int c, int pos,
-                                          const RopeFreq& rf) {
-  constexpr int TPR = D / 8;
+__device__ __forceinline__ float2 rope_entry(int pos, int i, const RopeFreq& rf) {
   constexpr double kTwoPi = 6.283185307179586476925286766559;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int i = c + TPR * k;
-    const double ang = (double)pos * rf.f[i];
-    const float r = (float)(ang - kTwoPi * rint(ang * (1.0 / kTwoPi)));  // in [-pi, pi]
-    float sn, cs;
-    sincosf(r, &sn, &cs);
-    row_cs[i] = make_float2(cs, sn);
+  const double ang = (double)pos * rf.f[i];
+  const float r = (float)(ang - kTwoPi * rint(ang * (1.0 / kTwoPi)));  // in [-pi, pi]
+  float sn, cs;
+  sincosf(r, &sn, &cs);
+  return make_float2(cs, sn);
+}
+
+template <int D, int ROWS>
+__device__ __forceinline__ void rope_fill_all(float2 (*s_cs)[D / 2], int64_t t_a, int ntok,
+                                              const int32_t* __restrict__ pos,
+                                              const RopeFreq& rf) {
+  for (int j = threadIdx.x; j < ntok * (D / 2); j += blockDim.x) {
+    const int k = j / (D / 2), i = j % (D / 2);
+    s_cs[k][i] = rope_entry<D>(pos[t_a + k], i, rf);
   }
+  __syncthreads();
 }
 
 // Rotate the 8 values x (elements 8c .. 8c+7 of a D-wide row, c = lane's chunk) with the
@@ -91,7 +97,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
   const int g = (int)(r % Hkv);
 
   bool valid = in_range;
-  int pb = 0, slot = 0, rpos = 0;
+  int pb = 0, slot = 0;
   if (valid) {
     int b, p;
     if constexpr (VARLEN) {
@@ -107,7 +113,6 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
       b = seq_idx[t];
       p = pos[t];
     }
-    rpos = p;
     valid = b >= 0 && b < num_seqs && p >= 0 && p < max_blocks * bs;
     if (valid) {
       pb = table[(int64_t)b * max_blocks + p / bs];
@@ -122,13 +127,13 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     win[0] = *reinterpret_cast<const u32x4*>(k_new + src);
     win[1] = *reinterpret_cast<const u32x4*>(v_new + src);
   }
-  int cs_row = 0;  // this row's token's table: its first row inside the workgroup
+  int cs_row = 0;  // this row's token's table
   if constexpr (ROPE) {
+    static_assert(!VARLEN, "RoPE append takes explicit positions");
     const int64_t r0 = (int64_t)blockIdx.x * ROWS;
-    const int64_t first = t * Hkv > r0 ? t * Hkv : r0;
-    cs_row = (int)(first - r0);
-    if (in_range && r == first) rope_fill<D>(s_cs[cs_row], c, rpos, rf);
-    __syncthreads();
+    const int64_t t_a = r0 / Hkv, t_b = (min(r0 + ROWS, rows) - 1) / Hkv;
+    cs_row = in_range ? (int)(t - t_a) : 0;  // rows past the end read entry 0, store nothing
+    rope_fill_all<D, ROWS>(s_cs, t_a, (int)(t_b - t_a + 1), pos, rf);
   }
 
 #pragma unroll
@@ -210,10 +215,9 @@ __global__ __launch_bounds__(256) void rope_rows_kernel(uint16_t* __restrict__ x
   uint16_t* p = x + r * D + 8 * c;
   if (in_range) w = *reinterpret_cast<const u32x4*>(p);
   const int64_t t = r / H, r0 = (int64_t)blockIdx.x * ROWS;
-  const int64_t first = t * H > r0 ? t * H : r0;  // the token's first row in the workgroup
-  const int cs_row = (int)(first - r0);
-  if (in_range && r == first) rope_fill<D>(s_cs[cs_row], c, pos[t], rf);
-  __syncthreads();
+  const int64_t t_a = r0 / H, t_b = (min(r0 + ROWS, rows) - 1) / H;
+  const int cs_row = in_range ? (int)(t - t_a) : 0;  // rows past the end store nothing
+  rope_fill_all<D, ROWS>(s_cs, t_a, (int)(t_b - t_a + 1), pos, rf);
   float v[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
