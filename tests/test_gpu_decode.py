@@ -137,6 +137,18 @@ def test_decode_balanced_tiny_and_empty_contexts(kv):
     assert maxabs(got[live], ro) <= BF16_TOL
 
 
+@pytest.mark.parametrize("Hq", [4, 8])
+def test_decode_one_long_sequence_split_over_every_wave(Hq):
+    """One sequence, one KV head, 20000 keys: the balanced shape gives each of ~1250 waves a
+    single block, so the merge combines ~1250 partials of one segment (4 columns use the VALU
+    PV form, 8 the MFMA form)."""
+    wl, ctx, table, nb, qbits, qf = _small(64, Hq, 1, 0, ctx=(20000,), seed=13)
+    kb, vb = pool(wl, "k", nb), pool(wl, "v", nb)
+    o = _decode(dev_bf16(qbits), dev_bf16(kb), dev_bf16(vb), dev(table), dev(ctx), wl, 20000)
+    ro, _ = oracle.decode_paged(qf, bf16_value(kb), bf16_value(vb), table, ctx, wl.scale, 16)
+    assert maxabs(host_f64(o), ro) <= BF16_TOL
+
+
 def test_decode_large_batch_uses_fixed_splits():
     """Beyond the balanced shape's batch limit the default falls back to fixed splits."""
     rng = np.random.default_rng(5)
