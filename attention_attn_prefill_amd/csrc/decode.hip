@@ -1043,7 +1043,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
     if (e - wbase >= 64) {
       wbase += 64;
       ++wk;
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // window wk has landed
+      // Window wk's copy was issued 64 list positions (at least 32 chunks) ago, and every
+      // chunk since was computed after waiting for all loads older than the newest chunk's,
+      // so it has landed: no wait here (a vmcnt(0) would also drain the MFMA form's other
+      // chunk); the empty asm only keeps the compiler from reading the slice earlier.
+      asm volatile("" ::: "memory");
       tab = s_tab[wave][wk & 1][lane];
       if (wbase + 64 < end) fetch_window(wbase + 64, b, (wk + 1) & 1);
     }
@@ -1059,6 +1063,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
 
   W w;
   w.init(lane);
+  // MFMA form: the SIMD's issue arbiter favours older waves, so the workgroup dispatched first
+  // on a CU streams faster than the second one (INT8 70B-shaped decode: ~161 against ~180 us to
+  // finish the same work). The second half of the grid (the later workgroups) starts at
+  // priority 1 and every wave flips its priority every 4 chunks, so the two classes alternate.
+  int prio = W::kMfmaPv && blockIdx.x >= gridDim.x / 2 ? 1 : 0, nchunk = 0;
+  if (prio) __builtin_amdgcn_s_setprio(1);
   typename W::Chunk cA;
   auto prep = [&](typename W::Chunk& c, int j, int slot) {
 #pragma unroll
@@ -1069,6 +1079,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
     }
     c.t0 = j * BS;
     w.load(c, k_cache, v_cache, k_scale, v_scale, Hkv, g, s_lds[wave][slot]);
+    if (W::kMfmaPv && ((++nchunk) & 3) == 0) {
+      prio ^= 1;
+      if (prio) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);
+    }
   };
 
   w.load_q(q, b, g, G, QL, Hq, ctx, 0);
