@@ -24,6 +24,7 @@ constexpr int kKvBf16 = 0, kKvI8 = 1, kKvFp8 = 2;
 
 constexpr int kMaxSplitTokens = 8192;  // largest split_tokens a decode call accepts
 constexpr int kStreamMaxB = 2048;      // largest batch of the balanced decode shape
+constexpr int kMaxDevices = 64;        // devices with per-device launch state (attributes set once)
 
 struct DecodePlan {
   bool stream;           // balanced persistent shape (else fixed splits)

@@ -33,6 +33,7 @@
 //    the running max moves only when it grows by more than kRescaleSlack.
 #include "common.h"
 #include "launch.h"
+#include <atomic>
 #include <type_traits>
 
 namespace attn {
@@ -405,13 +406,16 @@ static void launch_d(const void* q, const void* k, const void* v, void* o, float
   const long long nwg = (long long)B * Hkv * n_hsub * n_qblk;
   const float scale_log2 = scale * kLog2e;
   const size_t lds = 2 * PTile<D>::STAGE;
-  // 64 KB of dynamic LDS at D=128 needs the opt-in; if it fails the launch fails and the
-  // entry point reports the launch error
-  static bool attr_set = false;
-  if (!attr_set)
-    attr_set = hipFuncSetAttribute((const void*)prefill_bf16_kernel<D, PAGED>,
-                                   hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   (int)lds) == hipSuccess;
+  // 64 KB of dynamic LDS at D=128 needs the opt-in, once per device; if it fails the launch
+  // fails and the entry point reports the launch error
+  static std::atomic<bool> attr_set[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  if (!attr_set[dev].load(std::memory_order_relaxed))
+    attr_set[dev].store(hipFuncSetAttribute((const void*)prefill_bf16_kernel<D, PAGED>,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                                            (int)lds) == hipSuccess,
+                        std::memory_order_relaxed);
   const int cus = device_cus();
   hipLaunchKernelGGL((prefill_bf16_kernel<D, PAGED>), dim3((unsigned)nwg), dim3(kPrefillThreads),
                      lds, stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
