@@ -77,14 +77,13 @@ __device__ __forceinline__ void rope8(float (&x)[8], int c, const float2* __rest
   }
 }
 
-template <int D, int KV, bool VARLEN, bool ROPE>
+template <int D, int KV, bool ROPE>
 __global__ __launch_bounds__(256) void kv_append_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ table, void* __restrict__ k_cache, void* __restrict__ v_cache,
     __half* __restrict__ k_scale, __half* __restrict__ v_scale, int64_t rows, int Hkv, int bs,
-    int num_seqs, int max_blocks, int num_blocks, const int32_t* __restrict__ cu_q,
-    const int32_t* __restrict__ ctx, RopeFreq rf) {
+    int num_seqs, int max_blocks, int num_blocks, RopeFreq rf) {
   constexpr int TPR = D / 8;        // threads per (token, head) row
   constexpr int ROWS = 256 / TPR;   // rows per workgroup
   __shared__ float2 s_cs[ROPE ? ROWS : 1][ROPE ? D / 2 : 1];
@@ -99,20 +98,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
   bool valid = in_range;
   int pb = 0, slot = 0;
   if (valid) {
-    int b, p;
-    if constexpr (VARLEN) {
-      int lo = 0, hi = num_seqs;  // largest b with cu_q[b] <= t
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (cu_q[mid] <= t) lo = mid; else hi = mid - 1;
-      }
-      b = lo;
-      const int q_len = b < num_seqs ? cu_q[b + 1] - cu_q[b] : 0;
-      p = b < num_seqs ? ctx[b] - q_len + (int)(t - cu_q[b]) : -1;
-    } else {
-      b = seq_idx[t];
-      p = pos[t];
-    }
+    const int b = seq_idx[t], p = pos[t];
     valid = b >= 0 && b < num_seqs && p >= 0 && p < max_blocks * bs;
     if (valid) {
       pb = table[(int64_t)b * max_blocks + p / bs];
@@ -129,7 +115,6 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
   }
   int cs_row = 0;  // this row's token's table
   if constexpr (ROPE) {
-    static_assert(!VARLEN, "RoPE append takes explicit positions");
     const int64_t r0 = (int64_t)blockIdx.x * ROWS;
     const int64_t t_a = r0 / Hkv, t_b = (min(r0 + ROWS, rows) - 1) / Hkv;
     cs_row = in_range ? (int)(t - t_a) : 0;  // rows past the end read entry 0, store nothing
@@ -236,9 +221,8 @@ static RopeFreq rope_freq(int D, double base) {
   return rf;
 }
 
-template <bool VARLEN, bool ROPE>
-static int launch_append(const AppendArgs& a, const int32_t* cu_q, const int32_t* ctx,
-                         double rope_base, hipStream_t stream) {
+template <bool ROPE>
+static int launch_append(const AppendArgs& a, double rope_base, hipStream_t stream) {
   const RopeFreq rf = ROPE ? rope_freq(a.D, rope_base) : RopeFreq{};
   const int64_t rows = (int64_t)a.T * a.Hkv;
   const int tpr = a.D / 8;
@@ -247,11 +231,11 @@ static int launch_append(const AppendArgs& a, const int32_t* cu_q, const int32_t
   const int64_t grid = (threads + block - 1) / block;
   if (grid == 0) return 0;
 #define ATTN_APPEND(DD, KV)                                                                    \
-  hipLaunchKernelGGL((kv_append_kernel<DD, KV, VARLEN, ROPE>), dim3((unsigned)grid), dim3(block), \
+  hipLaunchKernelGGL((kv_append_kernel<DD, KV, ROPE>), dim3((unsigned)grid), dim3(block),       \
                      0, stream, (const uint16_t*)a.k_new, (const uint16_t*)a.v_new, a.seq_idx,  \
                      a.pos, a.block_table, a.k_cache, a.v_cache, (__half*)a.k_scale,            \
                      (__half*)a.v_scale, rows, a.Hkv, a.block_size, a.num_seqs,                 \
-                     a.max_blocks_per_seq, a.num_blocks, cu_q, ctx, rf)
+                     a.max_blocks_per_seq, a.num_blocks, rf)
   if (a.D == 64) {
     if (a.kv == kKvI8) ATTN_APPEND(64, kKvI8); else if (a.kv == kKvFp8) ATTN_APPEND(64, kKvFp8); else ATTN_APPEND(64, kKvBf16);
   } else {
@@ -262,16 +246,11 @@ static int launch_append(const AppendArgs& a, const int32_t* cu_q, const int32_t
 }
 
 int launch_kv_append(const AppendArgs& a, hipStream_t stream) {
-  return launch_append<false, false>(a, nullptr, nullptr, 0.0, stream);
-}
-
-int launch_kv_append_varlen(const AppendArgs& a, const int32_t* cu_q, const int32_t* ctx,
-                            hipStream_t stream) {
-  return launch_append<true, false>(a, cu_q, ctx, 0.0, stream);
+  return launch_append<false>(a, 0.0, stream);
 }
 
 int launch_kv_append_rope(const AppendArgs& a, double rope_base, hipStream_t stream) {
-  return launch_append<false, true>(a, nullptr, nullptr, rope_base, stream);
+  return launch_append<true>(a, rope_base, stream);
 }
 
 int launch_rope_rows(void* x, const int32_t* pos, int T, int H, int D, double rope_base,

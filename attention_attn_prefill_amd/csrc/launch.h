@@ -92,10 +92,6 @@ int launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 int launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 int launch_decode(const DecodeArgs& a, hipStream_t stream);
 int launch_kv_append(const AppendArgs& a, hipStream_t stream);
-// Append rows of a packed chunk: row r of sequence b (cu_q[b] <= r < cu_q[b+1]) goes to
-// position ctx[b] - (cu_q[b+1] - cu_q[b]) + (r - cu_q[b]). a.seq_idx / a.pos are unused.
-int launch_kv_append_varlen(const AppendArgs& a, const int32_t* cu_q, const int32_t* ctx,
-                            hipStream_t stream);
 int launch_kv_append_rope(const AppendArgs& a, double rope_base, hipStream_t stream);
 int launch_rope_rows(void* x, const int32_t* pos, int T, int H, int D, double rope_base,
                      hipStream_t stream);

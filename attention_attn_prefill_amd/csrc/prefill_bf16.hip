@@ -84,12 +84,19 @@ __device__ __forceinline__ int v_swz(int row) {
 
 // Paged mode (chunked prefill): queries are packed rows, sequence b owning rows
 // cu_q[b] .. cu_q[b+1]-1, which are the last positions of its ctx[b] keys (bottom-right
-// alignment); K/V come from the paged cache through the block table.
+// alignment); K/V come from the paged cache through the block table. With k_new / v_new the
+// chunk's own K/V rows (packed like the queries) are written into the cache by the same
+// launch, and the chunk's keys are read from those rows rather than from the slots being
+// written, so no workgroup depends on another's writes.
 struct PagedArgs {
   const int32_t* cu_q;
   const int32_t* ctx;
   const int32_t* table;
   int max_blocks, num_blocks;
+  const uint16_t* k_new;  // [total_q][Hkv][D] or null
+  const uint16_t* v_new;
+  uint16_t* k_cache;  // the caches again, for the chunk's slots (written, never read here)
+  uint16_t* v_cache;
 };
 
 template <int D, bool PAGED>
@@ -217,8 +224,20 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(
         int pb = lb < pg_nblk ? trow[lb] : 0;  // blocks past the context: any valid block
         if (pb < 0 || pb >= pg.num_blocks) pb = 0;  // unusable entry: never dereferenced
         const int64_t boff = ((int64_t)pb * Hkv + g) * 16 * D;
-        lds_dma_16(k + boff + pg_slot_k, lds_addr(kdst + i * 4096));
-        lds_dma_16(v + boff + pg_slot_v, lds_addr(vdst + i * 4096));
+        const uint16_t* ks = k + boff + pg_slot_k;
+        const uint16_t* vs = v + boff + pg_slot_v;
+        if (pg.k_new != nullptr && k0 + kBN > off) {
+          // the chunk's own keys (positions off ..) come from its rows; keys past the
+          // context read the last row (their scores are masked, their V rows zeroed)
+          const int key = k0 + ld_row0 + i * ROW_STEP;
+          if (key >= off) {
+            const int64_t nrow = ((int64_t)(q_row0 + min(key, Lk - 1) - off) * Hkv + g) * D;
+            ks = pg.k_new + nrow + 8 * ld_kchunk;
+            vs = pg.v_new + nrow + 8 * ld_vchunk;
+          }
+        }
+        lds_dma_16(ks, lds_addr(kdst + i * 4096));
+        lds_dma_16(vs, lds_addr(vdst + i * 4096));
       }
     } else if (k0 + kBN <= S) {
       const uint16_t* kt = kbase + (int64_t)k0 * kv_row_stride;
@@ -343,6 +362,32 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(
 
   if (jlo <= jhi) issue_tile(jlo, 0);
 
+  if constexpr (PAGED) {
+    // The chunk's rows of this workgroup (one head sub-group per KV head writes) go to their
+    // cache slots, positions off + i: a bit copy, 16 bytes per thread step. Entries outside
+    // [0, num_blocks) are skipped.
+    if (pg.k_new != nullptr && hsub == 0) {
+      const int n = min(q0 + rows, Sq) - q0;
+      const int32_t* trow = pg.table + (int64_t)b * pg.max_blocks;
+      for (int c = tid; c < n * T::CHUNKS; c += kPrefillThreads) {
+        const int i = q0 + c / T::CHUNKS, ch = c % T::CHUNKS;
+        const int p = off + i;
+        // the row loads go out with the table load (one round trip, not two): the empty asm
+        // passes all three on, so no load is sunk behind the test of the entry
+        const int64_t src = ((int64_t)(q_row0 + i) * Hkv + g) * D + 8 * ch;
+        u32x4 kw = *reinterpret_cast<const u32x4*>(pg.k_new + src);
+        u32x4 vw = *reinterpret_cast<const u32x4*>(pg.v_new + src);
+        int pb = trow[p >> 4];
+        asm volatile("" : "+v"(pb), "+v"(kw), "+v"(vw));
+        if (pb >= 0 && pb < pg.num_blocks) {
+          const int64_t dst = (((int64_t)pb * Hkv + g) * 16 + (p & 15)) * D + 8 * ch;
+          *reinterpret_cast<u32x4*>(pg.k_cache + dst) = kw;
+          *reinterpret_cast<u32x4*>(pg.v_cache + dst) = vw;
+        }
+      }
+    }
+  }
+
   for (int j = jlo; j <= jhi; ++j) {
     const int st = (j - jlo) & 1;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile-j loads have landed
@@ -424,7 +469,7 @@ static void launch_d(const void* q, const void* k, const void* v, void* o, float
 }
 
 int launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
-  const PagedArgs none{nullptr, nullptr, nullptr, 0, 0};
+  const PagedArgs none{nullptr, nullptr, nullptr, 0, 0, nullptr, nullptr, nullptr, nullptr};
   if (a.D == 64)
     launch_d<64, false>(a.q, a.k, a.v, a.o, a.lse, a.B, a.S, a.Hq, a.Hkv, a.scale, a.causal,
                         a.window, none, stream);
@@ -435,13 +480,16 @@ int launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
 }
 
 int launch_prefill_paged(const PrefillPagedArgs& a, hipStream_t stream) {
-  if (a.k_new != nullptr) {
-    AppendArgs ap{a.k_new, a.v_new, nullptr, nullptr, a.table, a.k_cache, a.v_cache, nullptr,
-                  nullptr, kKvBf16, a.total_q, a.Hkv, a.D, 16, a.B, a.max_blocks_per_seq,
-                  a.num_blocks};
-    launch_kv_append_varlen(ap, a.cu_q, a.ctx, stream);
-  }
-  const PagedArgs pg{a.cu_q, a.ctx, a.table, a.max_blocks_per_seq, a.num_blocks};
+  // one launch: the chunk's K/V rows are written into the cache by the attention kernel
+  const PagedArgs pg{a.cu_q,
+                     a.ctx,
+                     a.table,
+                     a.max_blocks_per_seq,
+                     a.num_blocks,
+                     (const uint16_t*)a.k_new,
+                     (const uint16_t*)a.v_new,
+                     (uint16_t*)a.k_cache,
+                     (uint16_t*)a.v_cache};
   if (a.D == 64)
     launch_d<64, true>(a.q, a.k_cache, a.v_cache, a.o, a.lse, a.B, a.max_q_len, a.Hq, a.Hkv,
                        a.scale, a.causal, a.window, pg, stream);

@@ -201,7 +201,8 @@ def time_chunked(t, A, reps: int):
     ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
     fl = chunked_flops()
     tf = fl / (ms * 1e-3) / 1e12
-    return {"kernel": "attn_prefill_paged (varlen append + paged bf16 MFMA prefill)", "ms": ms,
+    return {"kernel": "attn_prefill_paged (paged bf16 MFMA prefill, append in the same launch)",
+            "ms": ms,
             "TFLOP/s": tf, "frac_mfma_peak": tf / BF16_PEAK_TFLOPS, "algorithmic_flops": fl,
             "tokens_per_s": c["B"] * c["q_len"] / (ms * 1e-3), "calls": reps,
             "workload": f"B={c['B']} chunks of {c['q_len']} rows after {c['ctx'] - c['q_len']}-token "

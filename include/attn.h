@@ -88,8 +88,11 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, float* ls
  *  q, o         : [total_q][Hq][D] bf16, packed: sequence b owns rows cu_q[b] .. cu_q[b+1]-1.
  *  k_new, v_new : [total_q][Hkv][D] bf16, the chunk's keys and values, written (bit copy) to
  *                 positions context_lens[b] - q_len_b .. context_lens[b] - 1 of sequence b
- *                 (q_len_b = cu_q[b+1] - cu_q[b]) before attention runs; both NULL when the
- *                 cache already holds them.
+ *                 (q_len_b = cu_q[b+1] - cu_q[b]) by the same launch that computes attention,
+ *                 which reads the chunk's own keys from these rows; both NULL when the cache
+ *                 already holds them. The slots of those positions must not also hold a key
+ *                 that any sequence of the call reads from the cache (a table that maps
+ *                 distinct positions to distinct slots guarantees this).
  *  k_cache,
  *  v_cache      : bf16 [num_blocks][Hkv][block_size][D], block_table int32
  *                 [B][max_blocks_per_seq], as in attn_decode_paged.

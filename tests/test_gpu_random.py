@@ -7,9 +7,9 @@ import numpy as np
 import pytest
 
 import oracle
-from synth import (DecodeWorkload, PrefillWorkload, bf16_value, fp8_pool, int8_pool, new_tokens,
-                   paged_table, pool, prefill_inputs)
-from tests.gpu_util import BF16_TOL, dev, dev_bf16, host_f64, maxabs, torch
+from synth import (DecodeWorkload, PrefillWorkload, bf16_bits, bf16_value, fp8_pool, int8_pool,
+                   new_tokens, paged_table, pool, prefill_inputs)
+from tests.gpu_util import BF16_TOL, dev, dev_bf16, host_bits, host_f64, maxabs, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -154,13 +154,17 @@ def test_random_prefill_paged(c):
     cu = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
     seq = np.repeat(np.arange(len(ctx)), ql).astype(np.int32)
     pos = np.concatenate([np.arange(n - q, n) for n, q in zip(ctx, ql)]).astype(np.int32)
-    o = A.attn_prefill_paged(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), dev(table), dev(cu), dev(ctx),
+    kc, vc = dev_bf16(kb), dev_bf16(vb)
+    o = A.attn_prefill_paged(dev_bf16(qb), kc, vc, dev(table), dev(cu), dev(ctx),
                              max(1, int(ql.max())), scale=D ** -0.5, causal=True, window=window,
                              k_new=dev_bf16(kn), v_new=dev_bf16(vn))
     t.cuda.synchronize()
-    if T == 0:
-        return
     kexp = oracle.append_expected(bf16_value(kb), bf16_value(kn), seq, pos, table, 16)
     vexp = oracle.append_expected(bf16_value(vb), bf16_value(vn), seq, pos, table, 16)
+    # the chunk's rows land in the cache bit for bit, every other slot is untouched
+    assert np.array_equal(host_bits(kc), bf16_bits(kexp))
+    assert np.array_equal(host_bits(vc), bf16_bits(vexp))
+    if T == 0:
+        return
     ro, _ = oracle.prefill_paged(qf, cu, kexp, vexp, table, ctx, D ** -0.5, 16, True, window)
     assert maxabs(host_f64(o), ro) <= BF16_TOL
