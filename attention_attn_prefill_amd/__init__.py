@@ -121,7 +121,7 @@ def attn_prefill_paged(q, k_cache, v_cache, block_table, cu_q, context_lens, max
                        k_new=None, v_new=None, scale: float | None = None, causal: bool = True,
                        window: int = 0, out=None, lse=None):
     """Chunked prefill over a paged cache (bf16). q [total_q][Hq][D] packed by cu_q [B+1];
-    k_new/v_new [total_q][Hkv][D] are written into the cache first when given."""
+    k_new/v_new [total_q][Hkv][D], when given, are written into the cache by the same launch."""
     import torch
     total_q, Hq, D = q.shape
     num_blocks, Hkv, bs, _ = k_cache.shape
