@@ -82,7 +82,7 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, float* ls
 
 /*
  * attn_prefill_paged -- chunked (continued) prefill over a paged KV cache, with the chunk's
- * K/V written into the cache first. [TI] "分页KV缓存：借鉴操作系统的内存管理" (paged cache) and
+ * K/V written into the cache by the same launch. [TI] "分页KV缓存：借鉴操作系统的内存管理" (paged cache) and
  * "Flash Attention：内存与计算的重平衡" (tiled attention with an online softmax); window: [IL].
  *
  *  q, o         : [total_q][Hq][D] bf16, packed: sequence b owns rows cu_q[b] .. cu_q[b+1]-1.
