@@ -13,7 +13,7 @@
 //  * A workgroup is 4 waves; a wave owns 32 query rows of one head. The waves of a workgroup
 //    are the query heads that share one KV head (GQA) and/or consecutive 32-row chunks, so one
 //    K/V tile in LDS serves 128 query rows.
-//  * K and V tiles (64 keys) move from global memory straight into LDS with
+//  * K and V tiles (64 keys at D=64, 32 at D=128) move from global memory straight into LDS with
 //    global_load_lds_dwordx4 (no register staging), double-buffered: the next tile's loads are
 //    in flight while the current tile is computed; one barrier per tile. Both tiles keep their
 //    natural [key][d] rows; 16-byte chunks are XOR-swizzled by key so the MFMA operand reads
@@ -39,7 +39,10 @@
 namespace attn {
 
 constexpr int kPrefillThreads = 256;
-constexpr int kBN = 64;  // keys per tile
+// keys per tile: 64 at D=64; 32 at D=128, which halves the LDS and score registers per
+// workgroup so that three waves fit on a SIMD
+template <int D>
+constexpr int kTileKeys = D == 128 ? 32 : 64;
 // The running max lags the true max by at most this much (log2 units), so probabilities stay
 // below 2^kRescaleSlack; O and l share the same reference, so o = O / l is unchanged.
 constexpr float kRescaleSlack = 8.0f;
@@ -63,7 +66,8 @@ template <int D>
 struct PTile {
   static constexpr int ROWB = D * 2;                 // bytes of one K or V row
   static constexpr int CHUNKS = ROWB / 16;           // 16-byte chunks per row
-  static constexpr int TILE = kBN * ROWB;            // bytes of one K (or V) tile
+  static constexpr int BN = kTileKeys<D>;            // keys per tile
+  static constexpr int TILE = BN * ROWB;             // bytes of one K (or V) tile
   static constexpr int STAGE = 2 * TILE;             // K tile then V tile
   static constexpr int INSTR = TILE / 1024;          // wave load instructions per tile
   static constexpr int PER_WAVE = INSTR / 4;         // ... per wave
@@ -100,12 +104,13 @@ struct PagedArgs {
 };
 
 template <int D, bool PAGED>
-__global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(
+__global__ __launch_bounds__(kPrefillThreads, D == 128 ? 3 : 2) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int S,
     int Hq, int Hkv, int G, int HW, int QW, int n_qblk, int n_hsub, float scale_log2,
     int causal, int window, int cpx, PagedArgs pg) {
   using T = PTile<D>;
+  constexpr int kBN = T::BN;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -451,8 +456,8 @@ static void launch_d(const void* q, const void* k, const void* v, void* o, float
   const long long nwg = (long long)B * Hkv * n_hsub * n_qblk;
   const float scale_log2 = scale * kLog2e;
   const size_t lds = 2 * PTile<D>::STAGE;
-  // 64 KB of dynamic LDS at D=128 needs the opt-in, once per device; if it fails the launch
-  // fails and the entry point reports the launch error
+  // the dynamic-LDS limit is raised to this launch's size once per device (a no-op below the
+  // default); if that fails the launch fails and the entry point reports the launch error
   static std::atomic<bool> attr_set[kMaxDevices];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
