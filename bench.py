@@ -182,6 +182,11 @@ def chunked_flops() -> float:
     return 4.0 * c["D"] * c["Hq"] * c["B"] * pairs
 
 
+def _pct(x) -> dict:
+    """p10 / p50 / p90 of per-call times (ms)."""
+    return {f"p{q}": float(np.percentile(x, q)) for q in (10, 50, 90)}
+
+
 def time_chunked(t, A, reps: int):
     """attn_prefill_paged with fused append, timed per call with events (outside the step)."""
     C = setup_chunked(t)
@@ -198,11 +203,12 @@ def time_chunked(t, A, reps: int):
         call()
         e1.record()
     t.cuda.synchronize()
-    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    per = [e0.elapsed_time(e1) for e0, e1 in ev]
+    ms = float(np.mean(per))
     fl = chunked_flops()
     tf = fl / (ms * 1e-3) / 1e12
     return {"kernel": "attn_prefill_paged (paged bf16 MFMA prefill, append in the same launch)",
-            "ms": ms,
+            "ms": ms, "ms_percentiles": _pct(per),
             "TFLOP/s": tf, "frac_mfma_peak": tf / BF16_PEAK_TFLOPS, "algorithmic_flops": fl,
             "tokens_per_s": c["B"] * c["q_len"] / (ms * 1e-3), "calls": reps,
             "workload": f"B={c['B']} chunks of {c['q_len']} rows after {c['ctx'] - c['q_len']}-token "
@@ -235,11 +241,12 @@ def time_decode_multi(t, A, dwl, Dd, reps: int, q_len: int = 4):
         e1.record()
         t.cuda.synchronize()
         ms.append(e0.elapsed_time(e1))
-    ms = float(np.mean(ms))
+    per, ms = ms, float(np.mean(ms))
     # algorithmic bytes: the visible K/V once (as single-token decode) plus q_len x Q and O
     byts = decode_bytes(dwl, Dd["ctx_np"]) + 2.0 * dwl.B * (q_len - 1) * dwl.Hq * dwl.D * 2
     gbs = byts / (ms * 1e-3) / 1e9
-    return {"kernel": "attn_decode_paged_multi", "q_len": q_len, "ms": ms, "GB/s": gbs,
+    return {"kernel": "attn_decode_paged_multi", "q_len": q_len, "ms": ms, "ms_percentiles": _pct(per),
+            "GB/s": gbs,
             "frac_hbm_peak": gbs / HBM_PEAK_GBS, "algorithmic_bytes": byts,
             "tokens_per_s": dwl.B * q_len / (ms * 1e-3), "calls": reps,
             "workload": f"{dwl.name} cache, {q_len} draft rows per sequence, causal among them"}
@@ -271,10 +278,12 @@ def time_append_rope(t, A, reps: int):
         call()
         e1.record()
     t.cuda.synchronize()
-    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    per = [e0.elapsed_time(e1) for e0, e1 in ev]
+    ms = float(np.mean(per))
     byts = 4.0 * T * Hkv * D * 2 + 2.0 * T * 4  # K, V read and written; seq, pos read
     gbs = byts / (ms * 1e-3) / 1e9
-    return {"kernel": "kv_cache_append_rope", "ms": ms, "GB/s": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS,
+    return {"kernel": "kv_cache_append_rope", "ms": ms, "ms_percentiles": _pct(per), "GB/s": gbs,
+            "frac_hbm_peak": gbs / HBM_PEAK_GBS,
             "algorithmic_bytes": byts, "calls": reps,
             "workload": f"{T} tokens ({B} x {S}), Hkv={Hkv} D={D} bf16, RoPE base 500000, permuted pool"}
 
@@ -313,10 +322,11 @@ def time_decode_fp8(t, A, dwl, Dd, reps: int):
         e1.record()
         t.cuda.synchronize()
         ms.append(e0.elapsed_time(e1))
-    ms = float(np.mean(ms))
+    per, ms = ms, float(np.mean(ms))
     byts = decode_bytes(dataclasses.replace(dwl, kv_dtype="fp8"), Dd["ctx_np"])
     gbs = byts / (ms * 1e-3) / 1e9
-    return {"kernel": "attn_decode_paged (FP8 E4M3 cache)", "ms": ms, "GB/s": gbs,
+    return {"kernel": "attn_decode_paged (FP8 E4M3 cache)", "ms": ms, "ms_percentiles": _pct(per),
+            "GB/s": gbs,
             "frac_hbm_peak": gbs / HBM_PEAK_GBS, "algorithmic_bytes": byts, "calls": reps,
             "tokens_per_s": dwl.B / (ms * 1e-3),
             "workload": f"{dwl.name} shapes with the cache quantized to FP8 E4M3 + fp16 per-token scales"}
