@@ -2,7 +2,10 @@
 combination of head dim, head counts, batch, ragged and empty contexts, window, cache dtype,
 split policy and draft rows (decode), or batch, length, heads, mask and window (prefill), so
 combinations no hand-written case names are exercised too. Sizes stay small enough for the
-oracle; every draw is printed in the test id."""
+oracle; every draw is printed in the test id. ATTN_RANDOM_SCALE=k multiplies the number of cases
+(k = 1 by default), for a longer sweep run by hand."""
+import os
+
 import numpy as np
 import pytest
 
@@ -38,7 +41,8 @@ def _decode_case(i):
                 seed=9000 + i)
 
 
-DECODE_CASES = [_decode_case(i) for i in range(60)]
+SCALE = max(1, int(os.environ.get("ATTN_RANDOM_SCALE", "1")))
+DECODE_CASES = [_decode_case(i) for i in range(60 * SCALE)]
 
 
 def _dec_id(c):
@@ -100,7 +104,7 @@ def _prefill_case(i):
     return dict(D=D, Hkv=Hkv, G=G, B=B, S=S, causal=causal, window=window, seed=9500 + i)
 
 
-PREFILL_CASES = [_prefill_case(i) for i in range(40)]
+PREFILL_CASES = [_prefill_case(i) for i in range(40 * SCALE)]
 
 
 @pytest.mark.parametrize("c", PREFILL_CASES,
@@ -133,7 +137,7 @@ def _chunk_case(i):
     return dict(D=D, Hkv=Hkv, G=G, ctx=tuple(ctx), ql=tuple(ql), window=window, seed=9800 + i)
 
 
-CHUNK_CASES = [_chunk_case(i) for i in range(30)]
+CHUNK_CASES = [_chunk_case(i) for i in range(30 * SCALE)]
 
 
 @pytest.mark.parametrize("c", CHUNK_CASES,
