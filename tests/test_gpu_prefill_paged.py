@@ -93,6 +93,23 @@ def test_prefill_paged_without_append_and_non_causal():
         assert maxabs(host_f64(o), ro) <= BF16_TOL
 
 
+@pytest.mark.parametrize("D,window", [(64, 0), (128, 0), (64, 37), (128, 200)])
+def test_prefill_paged_fused_append_reads_what_the_cache_holds(D, window):
+    # The fused call takes the chunk's keys from k_new / v_new while it writes them to the
+    # cache; a second call without k_new reads the same values from the cache. Same bf16 inputs
+    # in the same order, so O and the LSE must agree bit for bit.
+    c = _case((300, 61, 17), (100, 61, 17), 8, 2, D, seed=4242 + D + window)
+    o1, L1, kc, vc = _run(c, window)
+    import attention_attn_prefill_amd as A
+    t = torch()
+    L2 = t.empty_like(L1)
+    o2 = A.attn_prefill_paged(dev_bf16(c["qb"]), kc, vc, dev(c["table"]), dev(c["cu"]), dev(c["ctx"]),
+                              int(c["q_len"].max()), scale=c["scale"], causal=True, window=window, lse=L2)
+    t.cuda.synchronize()
+    assert np.array_equal(host_bits(o1), host_bits(o2))
+    assert np.array_equal(L1.cpu().numpy().view(np.uint32), L2.cpu().numpy().view(np.uint32))
+
+
 def test_prefill_paged_whole_sequence_equals_contiguous_prefill():
     """A chunk covering the whole sequence is ordinary prefill: compare with attn_prefill."""
     import attention_attn_prefill_amd as A
