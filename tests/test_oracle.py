@@ -566,3 +566,110 @@ def test_fp8_quantizer_bounds():
     assert (amax >= 416).all() and (amax <= 448).all()
     z, sz = oracle.quantize_fp8(np.zeros((2, 64), np.float32))
     assert (z == 0).all() and (sz == 0).all()
+
+
+# ---- scale rules of the byte caches, pinned by hand values --------------------------------------
+def test_fp8_quantizer_hand_values():
+    # absmax 1.0: fp32 1/448 = 0.00223214... is not an fp16 value; to nearest-even fp16 it is
+    # 2^-9 * (1 + 146/1024) = 0.0022315979 (bits 0x1892). 1.0 / s = 448.11, clamped to 448 -> 0x7E.
+    # x1 = 1.1875 * s exactly (11 + 5 significant bits), so x1 / s = 1.1875, the midpoint of
+    # 1.125 (0x39) and 1.25 (0x3A): the tie goes to the even code 0x3A. Divided by the unrounded
+    # fp32 1/448 instead it would be 1.18721 -> 0x39; a divisor other than 448 changes the scale.
+    # -0.5 / s = -224.05 -> -224 = -(1 + 6/8) * 2^7 -> 0xF6; 0 -> 0x00.
+    s_bits = 0x1892
+    s = float(np.uint16(s_bits).view(np.float16))
+    assert s == 2.0 ** -9 * (1 + 146 / 1024)
+    x = np.array([[1.0, 1.1875 * s, -0.5, 0.0]], np.float32)
+    codes, sc = oracle.quantize_fp8(x)
+    assert int(sc.view(np.uint16)[0]) == s_bits
+    assert codes.tolist() == [[0x7E, 0x3A, 0xF6, 0x00]]
+    # absmax 448 gives the scale 1 exactly, and then every code is the E4M3 value of x itself
+    codes, sc = oracle.quantize_fp8(np.array([[448.0, -3.0, 1.0625, 2.0 ** -9]], np.float32))
+    assert float(sc[0]) == 1.0 and codes.tolist() == [[0x7E, 0xC4, 0x38, 0x01]]
+
+
+def test_fp8_quantizer_scale_mutants_are_caught(monkeypatch):
+    import oracle.attn_fp64 as oa
+
+    def unrounded(x):  # divides by fp32 a / 448 instead of the stored fp16 scale
+        x = np.asarray(x, np.float32)
+        a = np.abs(x).max(axis=-1)
+        s32 = a / np.float32(448.0)
+        y = np.clip(x / s32[..., None], np.float32(-448.0), np.float32(448.0))
+        return oa.fp8_e4m3_encode(y.astype(np.float64)), s32.astype(np.float16)
+
+    def divisor_440(x):  # the rule with 440 in place of 448
+        x = np.asarray(x, np.float32)
+        s16 = (np.abs(x).max(axis=-1) / np.float32(440.0)).astype(np.float16)
+        y = np.clip(x / s16.astype(np.float32)[..., None], np.float32(-448.0), np.float32(448.0))
+        return oa.fp8_e4m3_encode(y.astype(np.float64)), s16
+
+    for mutant in (unrounded, divisor_440):
+        monkeypatch.setattr(oracle, "quantize_fp8", mutant)
+        with pytest.raises(AssertionError):
+            test_fp8_quantizer_hand_values()
+        monkeypatch.undo()
+
+
+def test_dequantize_hand_values():
+    # INT8: code * scale, exactly
+    codes = np.array([[127, -3, 0, 1]], np.int8)
+    assert oracle.dequantize_int8(codes, np.array([0.5], np.float16)).tolist() == [[63.5, -1.5, 0.0, 0.5]]
+    assert oracle.dequantize_int8(codes, np.array([2.0 ** -20], np.float16)).tolist() == \
+        [[127 * 2.0 ** -20, -3 * 2.0 ** -20, 0.0, 2.0 ** -20]]
+    # FP8: E4M3 value * scale (0x38 = 1, 0xC4 = -3, 0x01 = 2^-9, 0x7E = 448)
+    c8 = np.array([[0x38, 0xC4, 0x01, 0x7E]], np.uint8)
+    assert oracle.dequantize_fp8(c8, np.array([0.25], np.float16)).tolist() == [[0.25, -0.75, 2.0 ** -11, 112.0]]
+
+
+def _scaled_cache_case(bs=2, seed=31):
+    """A tiny INT8 paged cache with distinct fp16 scales per (block, head, slot) for K and V."""
+    rng = np.random.default_rng(seed)
+    ctx = np.array([5, 3, 1], np.int32)
+    table, nb = paged_table(ctx, bs, seed, 1, True)
+    Hkv, D = 2, 3
+    kc = rng.integers(-127, 128, (nb, Hkv, bs, D)).astype(np.int8)
+    vc = rng.integers(-127, 128, (nb, Hkv, bs, D)).astype(np.int8)
+    ks = (rng.uniform(0.5, 1.5, (nb, Hkv, bs)) / 100).astype(np.float16)
+    vs = (rng.uniform(0.5, 1.5, (nb, Hkv, bs)) / 50).astype(np.float16)
+    q = rng.standard_normal((3, 4, D))
+    return ctx, table, kc, vc, ks, vs, q
+
+
+@pytest.mark.parametrize("window", [0, 2])
+def test_decode_paged_scaled_branch_brute(window):
+    bs = 2
+    ctx, table, kc, vc, ks, vs, q = _scaled_cache_case(bs)
+    o, _ = oracle.decode_paged(q, kc, vc, table, ctx, 0.7, bs, window, k_scale=ks, v_scale=vs)
+    for b in range(len(ctx)):
+        n = int(ctx[b])
+        # the cache the attention sees, built here token by token: code * scale of its slot
+        kk = np.zeros((n, 2, 3))
+        vv = np.zeros((n, 2, 3))
+        for t in range(n):
+            pb, slot = int(table[b][t // bs]), t % bs
+            for g in range(2):
+                for d in range(3):
+                    kk[t, g, d] = float(kc[pb, g, slot, d]) * float(ks[pb, g, slot])
+                    vv[t, g, d] = float(vc[pb, g, slot, d]) * float(vs[pb, g, slot])
+        ob = _brute(q[b][None, None], kk[None], vv[None], 0.7, True, window)
+        assert np.abs(o[b] - ob[0, 0]).max() < 1e-12
+
+
+def test_decode_paged_scale_mutants_are_caught(monkeypatch):
+    orig = oracle.decode_paged
+
+    def k_scale_on_v(*a, k_scale=None, v_scale=None, **kw):
+        return orig(*a, k_scale=k_scale, v_scale=k_scale, **kw)
+
+    def v_scale_dropped(*a, k_scale=None, v_scale=None, **kw):
+        return orig(*a, k_scale=k_scale, v_scale=np.ones_like(v_scale), **kw)
+
+    def k_scale_dropped(*a, k_scale=None, v_scale=None, **kw):
+        return orig(*a, k_scale=np.ones_like(k_scale), v_scale=v_scale, **kw)
+
+    for mutant in (k_scale_on_v, v_scale_dropped, k_scale_dropped):
+        monkeypatch.setattr(oracle, "decode_paged", mutant)
+        with pytest.raises(AssertionError):
+            test_decode_paged_scaled_branch_brute(0)
+        monkeypatch.undo()
