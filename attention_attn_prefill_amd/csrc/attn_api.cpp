@@ -102,6 +102,10 @@ int attn_prefill_paged(const void* q, const void* k_new, const void* v_new, void
   if ((k_new == nullptr) != (v_new == nullptr))
     return fail(ATTN_ERR_NULL, "k_new and v_new must be both given or both NULL");
   if (total_q == 0 || max_q_len == 0) return ok();
+  // the grid is one-dimensional: its thread count must stay below 2^32
+  if (attn::prefill_workgroups(B, max_q_len, Hq, Hkv) * attn::prefill_threads_per_workgroup() >=
+      (1LL << 32))
+    return fail(ATTN_ERR_SHAPE, "B * Hq * max_q_len too large for one launch");
   if (!q || !k_cache || !v_cache || !block_table || !cu_q || !context_lens || !o)
     return fail(ATTN_ERR_NULL, "q, k_cache, v_cache, block_table, cu_q, context_lens and o are required");
   attn::PrefillPagedArgs a{q, k_new, v_new, k_cache, v_cache, block_table, cu_q, context_lens,

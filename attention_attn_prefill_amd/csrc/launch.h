@@ -97,4 +97,9 @@ int launch_rope_rows(void* x, const int32_t* pos, int T, int H, int D, double ro
                      hipStream_t stream);
 int launch_prefill_paged(const PrefillPagedArgs& a, hipStream_t stream);
 
+// Workgroups and threads per workgroup of a bf16 prefill launch over B sequences of up to S
+// query rows (the grid is one-dimensional).
+long long prefill_workgroups(int B, int S, int Hq, int Hkv);
+int prefill_threads_per_workgroup();
+
 }  // namespace attn

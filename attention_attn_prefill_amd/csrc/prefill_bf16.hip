@@ -443,13 +443,30 @@ __global__ __launch_bounds__(kPrefillThreads, D == 128 ? 3 : 2) void prefill_bf1
   }
 }
 
+// Query heads per workgroup (the waves of one workgroup share a KV head), 32-row chunks per
+// head, and the number of workgroups for B sequences of up to S query rows.
+static void prefill_split(int Hq, int Hkv, int& HW, int& QW) {
+  const int G = Hq / Hkv;
+  HW = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+  QW = 4 / HW;
+}
+
+long long prefill_workgroups(int B, int S, int Hq, int Hkv) {
+  int HW, QW;
+  prefill_split(Hq, Hkv, HW, QW);
+  const long long rows = 32LL * QW;
+  return (long long)B * Hkv * (Hq / Hkv / HW) * ((S + rows - 1) / rows);
+}
+
+int prefill_threads_per_workgroup() { return kPrefillThreads; }
+
 template <int D, bool PAGED>
 static void launch_d(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                      int S, int Hq, int Hkv, float scale, int causal, int window, PagedArgs pg,
                      hipStream_t stream) {
   const int G = Hq / Hkv;
-  const int HW = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;  // heads per workgroup
-  const int QW = 4 / HW;                                    // 32-row chunks per head
+  int HW, QW;  // heads per workgroup, 32-row chunks per head
+  prefill_split(Hq, Hkv, HW, QW);
   const int rows = 32 * QW;
   const int n_qblk = (S + rows - 1) / rows;  // S: rows per sequence (paged: the largest chunk)
   const int n_hsub = G / HW;

@@ -172,6 +172,8 @@ def _paged(**kw):
     (dict(tq=-1), A.ATTN_ERR_SHAPE), (dict(Hq=6, Hkv=4), A.ATTN_ERR_SHAPE), (dict(window=-1), A.ATTN_ERR_SHAPE),
     (dict(scale=-1.0), A.ATTN_ERR_SHAPE), (dict(D=96), A.ATTN_ERR_UNSUPPORTED), (dict(bs=32), A.ATTN_ERR_UNSUPPORTED),
     (dict(tq=0, q=None), A.ATTN_OK),
+    # 1024 sequences x 16 heads x 2^20 rows: 2^27 workgroups of 256 threads, past a 2^32-thread grid
+    (dict(B=1024, Hq=16, Hkv=16, mq=1 << 20, tq=1 << 30), A.ATTN_ERR_SHAPE),
 ])
 def test_prefill_paged_validation(kw, code):
     assert _paged(**kw) == code
