@@ -82,6 +82,19 @@ __device__ __forceinline__ uint32_t fp8x2_hi(uint32_t u) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(u, 1.0f, true));
 }
 
+// Byte caches run QK^T on fp16 MFMA, so each bf16 query column is brought into fp16 range
+// first: multiplied by 2^k, k chosen from the column's largest magnitude so that it lands in
+// [2^8, 2^9) (k clamped to [-126, 126]). The product is exact, every element within 2^-22 of
+// the column maximum stays an fp16 normal (exact), and 2^-k is folded into the score scale.
+// Without it a bf16 query element of magnitude >= 65520 would become inf, and elements below
+// 2^-24 would flush to zero.
+__device__ __forceinline__ int q_range_shift(float amax) {
+  if (!(amax > 0.f)) return 0;
+  const int e = (int)((__float_as_uint(amax) >> 23) & 0xff) - 127;  // floor(log2) for normals
+  return min(126, max(-126, 8 - e));
+}
+__device__ __forceinline__ float pow2i(int k) { return __uint_as_float((uint32_t)(k + 127) << 23); }
+
 // xor-16 / xor-32 lane partners within a wave
 __device__ __forceinline__ float max_x32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -130,6 +143,7 @@ struct DecodeWave {
   int lane, hq, grp, c8, ts;
   frag_t qf[SH::KSTEPS];
   float bias;     // INT8: 1152 * sum of this head's fp16 q values (the widened codes carry +1152)
+  float qscale;   // byte caches: 2^-k of this lane's column (its query was scaled by 2^k)
   float m_run;    // per head (lanes hq), log2 units
   float l_part;   // this lane's share of the row sum
   float ps_part;  // INT8: this lane's share of sum(p'), in the fp16 values used
@@ -154,23 +168,36 @@ struct DecodeWave {
     const uint16_t* qrow = q + (((int64_t)b * QL + r) * Hq + g * G + h) * D;
     qpos = ctx - QL + r;
     wlo = window > 0 ? qpos - window + 1 : INT_MIN;
+    u32x4 w[SH::KSTEPS];
 #pragma unroll
     for (int j = 0; j < SH::KSTEPS; ++j) {
       // bf16: step j covers d = 32j + 8*grp + e; INT8: one 16-byte load feeds steps 2jj,
       // 2jj+1 covering d = 64*jj + 16*grp + 8*sub + e.
       const int d0 = BYTE ? (64 * (j / 2) + 16 * grp + 8 * (j % 2)) : (32 * j + 8 * grp);
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (hq < ncol) w = *reinterpret_cast<const u32x4*>(qrow + d0);
-      if constexpr (BYTE) {
+      w[j] = (u32x4){0u, 0u, 0u, 0u};
+      if (hq < ncol) w[j] = *reinterpret_cast<const u32x4*>(qrow + d0);
+      if constexpr (!BYTE) qf[j] = __builtin_bit_cast(bf16x8, w[j]);
+    }
+    qscale = 1.f;
+    if constexpr (BYTE) {
+      float amax = 0.f;
+#pragma unroll
+      for (int j = 0; j < SH::KSTEPS; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[j][e])), fabsf(bf16_hi(w[j][e]))));
+      amax = fmaxf(amax, __shfl_xor(amax, 16));
+      amax = max_x32(amax);
+      const int k = q_range_shift(amax);
+      const float up = pow2i(k);
+      qscale = pow2i(-k);
+#pragma unroll
+      for (int j = 0; j < SH::KSTEPS; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          qf[j][2 * e] = (_Float16)bf16_lo(w[e]);
-          qf[j][2 * e + 1] = (_Float16)bf16_hi(w[e]);
+          qf[j][2 * e] = (_Float16)(bf16_lo(w[j][e]) * up);
+          qf[j][2 * e + 1] = (_Float16)(bf16_hi(w[j][e]) * up);
           qsum += (float)qf[j][2 * e] + (float)qf[j][2 * e + 1];
         }
-      } else {
-        qf[j] = __builtin_bit_cast(bf16x8, w);
-      }
     }
     if constexpr (I8) {
       qsum += __shfl_xor(qsum, 16);
@@ -244,6 +271,7 @@ struct DecodeWave {
     // ---- scores on MFMA -----------------------------------------------------------------
     float sc[U][4];
     float cmax = -INFINITY;
+    const float sl = BYTE ? scale_log2 * qscale : scale_log2;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
@@ -275,11 +303,11 @@ struct DecodeWave {
         const bool vis = c.okb[u] && t >= lo && t < hi && t <= qpos && t >= wlo;
         float s;
         if constexpr (I8)
-          s = (a4[i] - bias) * c.ksc[u][i] * scale_log2;
+          s = (a4[i] - bias) * c.ksc[u][i] * sl;
         else if constexpr (F8)
-          s = a4[i] * c.ksc[u][i] * scale_log2;
+          s = a4[i] * c.ksc[u][i] * sl;
         else
-          s = a4[i] * scale_log2;
+          s = a4[i] * sl;
         sc[u][i] = vis ? s : -INFINITY;
         cmax = fmaxf(cmax, sc[u][i]);
       }
@@ -477,6 +505,7 @@ struct DecodeWaveM {
   int lane, hq, grp;
   frag_t qf[KSTEPS];
   float bias;     // INT8: 1152 * sum of this column's fp16 q values
+  float qscale;   // byte caches: 2^-k of this lane's column (its query was scaled by 2^k)
   float m_run;    // this lane's column, log2 units
   float l_part;   // this lane's share of the column's row sum
   float ps_part;  // INT8: this lane's share of sum(p'), in the fp16 values used
@@ -499,21 +528,34 @@ struct DecodeWaveM {
     const uint16_t* qrow = q + (((int64_t)b * QL + r) * Hq + g * G + h) * D;
     qpos = ctx - QL + r;
     wlo = window > 0 ? qpos - window + 1 : INT_MIN;
+    u32x4 w[KSTEPS];
 #pragma unroll
     for (int j = 0; j < KSTEPS; ++j) {
       const int d0 = BF ? 32 * j + 8 * grp : 64 * (j / 2) + 16 * grp + 8 * (j % 2);
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (hq < ncol) w = *reinterpret_cast<const u32x4*>(qrow + d0);
-      if constexpr (BF) {
-        qf[j] = __builtin_bit_cast(bf16x8, w);
-      } else {
+      w[j] = (u32x4){0u, 0u, 0u, 0u};
+      if (hq < ncol) w[j] = *reinterpret_cast<const u32x4*>(qrow + d0);
+      if constexpr (BF) qf[j] = __builtin_bit_cast(bf16x8, w[j]);
+    }
+    qscale = 1.f;
+    if constexpr (!BF) {
+      float amax = 0.f;
+#pragma unroll
+      for (int j = 0; j < KSTEPS; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[j][e])), fabsf(bf16_hi(w[j][e]))));
+      amax = fmaxf(amax, __shfl_xor(amax, 16));
+      amax = max_x32(amax);
+      const int k = q_range_shift(amax);
+      const float up = pow2i(k);
+      qscale = pow2i(-k);
+#pragma unroll
+      for (int j = 0; j < KSTEPS; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          qf[j][2 * e] = (_Float16)bf16_lo(w[e]);
-          qf[j][2 * e + 1] = (_Float16)bf16_hi(w[e]);
+          qf[j][2 * e] = (_Float16)(bf16_lo(w[j][e]) * up);
+          qf[j][2 * e + 1] = (_Float16)(bf16_hi(w[j][e]) * up);
           qsum += (float)qf[j][2 * e] + (float)qf[j][2 * e + 1];
         }
-      }
     }
     if constexpr (I8) {
       qsum += __shfl_xor(qsum, 16);
@@ -585,6 +627,7 @@ struct DecodeWaveM {
     float sc[U][4];
     float cmax = -INFINITY;
     const bool okb = (grp >> 1) ? c.okb[1] : c.okb[0];  // the block of tokens 8grp .. 8grp+7
+    const float sl = BF ? scale_log2 : scale_log2 * qscale;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
@@ -617,11 +660,11 @@ struct DecodeWaveM {
         const bool vis = okb && t >= lo && t < hi && t <= qpos && t >= wlo;
         float s;
         if constexpr (I8)
-          s = (a4[i] - bias) * scale_of(c.ksc8, e) * scale_log2;
+          s = (a4[i] - bias) * scale_of(c.ksc8, e) * sl;
         else if constexpr (F8)
-          s = a4[i] * scale_of(c.ksc8, e) * scale_log2;
+          s = a4[i] * scale_of(c.ksc8, e) * sl;
         else
-          s = a4[i] * scale_log2;
+          s = a4[i] * sl;
         sc[u][i] = vis ? s : -INFINITY;
         cmax = fmaxf(cmax, sc[u][i]);
       }

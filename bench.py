@@ -1,22 +1,29 @@
 """Benchmark of the attention hot path on one MI355X.
 
-One step = one pass of the whole path on the Llama-3.2-1B-shaped workload:
-  1. kv_cache_append of the newest token of each of 64 sequences into the paged bf16 cache
-     (32 query heads, 8 KV heads, D = 64, block 16, contexts uniform in [512, 4096]),
-  2. a 512 MiB scratch read that evicts L2 and the Infinity Cache with clean lines (so the
-     decode reads its cache from HBM, and no dirty write-back overlaps it),
-  3. attn_decode_paged over that cache (split-KV + log-sum-exp merge),
-  4. attn_prefill: causal GQA prefill, batch 1, S = 4096, 32/8 heads, D = 64, bf16.
-Each call is bracketed by HIP events on the stream the library launches on. The headline
-`value` is the prefill TFLOP/s (algorithmic flops: visible (query, key) pairs x 4D) over the
-timed steps; the decode HBM GB/s (algorithmic bytes: each visible K/V byte once, plus Q and O)
-is reported beside it. `--workload swa` / `int8_70b` time the other configurations the same way.
-Outside the timed steps, the default run also times attn_prefill_paged (chunked prefill over
-the paged cache with fused append: 4 sequences, 1024-token chunks after 3072-token prefixes)
-attn_decode_paged_multi (4 draft rows per sequence on the decode cache) and
-kv_cache_append_rope (a 64k-token prompt written into a paged cache with RoPE on K) and
-attn_decode_paged over an FP8 E4M3 copy of the decode cache. `--workload fp8_70b` runs the
-INT8 70B-shaped decode with an FP8 cache instead.
+One step = one pass of the whole path over the configurations the targets are set on
+(default `--workload target`):
+  * for each decode workload -- INT8-KV paged decode on a 70B-shaped layer (B = 16, 64/8
+    heads, D = 128, context 32768), sliding-window paged decode (B = 32, 32/8 heads, D = 128,
+    context 16384, window 4096) and the Llama-3.2-1B-shaped paged decode (B = 64, 32/8 heads,
+    D = 64, contexts uniform in [512, 4096]): kv_cache_append of each sequence's newest token,
+    a 512 MiB scratch read that evicts L2 and the Infinity Cache with clean lines (so the
+    decode reads its cache from HBM and no dirty write-back overlaps it), attn_decode_paged
+    (split KV + log-sum-exp merge);
+  * attn_prefill on the long-context sliding-window prefill (B = 2, S = 16384, 32/8 heads,
+    D = 128, window 4096) and on the Llama-3.2-1B-shaped causal prefill (B = 1, S = 4096,
+    32/8 heads, D = 64).
+Each call is bracketed by HIP events on the stream the library launches on. `value` and
+`roofline` are the long-context prefill's TFLOP/s (algorithmic flops: visible (query, key) pairs
+x 4D); `roofline_decode` is the INT8 decode's HBM GB/s (algorithmic bytes: each visible K/V
+byte and scale once, plus Q and O); every other workload carries its own roofline object
+(`roofline_decode_swa`, `roofline_decode_llama1b`, `roofline_prefill_llama1b`) and its
+per-call entry under `prefill` / `decode`. `--workload llama1b | swa | int8_70b | fp8_70b` run
+subsets (for profiling). Outside the timed steps, the default run also times
+attn_prefill_paged (chunked prefill over the paged cache with fused append: 4 sequences,
+1024-token chunks after 3072-token prefixes), attn_decode_paged_multi (4 draft rows per
+sequence on the Llama-shaped cache), kv_cache_append_rope (a 64k-token prompt written into a
+paged cache with RoPE on K) and attn_decode_paged over an FP8 E4M3 copy of the Llama-shaped
+cache.
 
 Before touching the GPU, bench.py runs attention_attn_prefill_amd/attn_peaks (built with the
 library) as a child process: a bf16 MFMA-only loop (with the shader clock it ran at), an HBM
@@ -24,8 +31,8 @@ streaming read and a random 2 KB-block gather; the JSON line carries them as
 `measured_peaks`, and each roofline object adds `frac_of_measured` beside the fraction of the
 published peak. Per-call times also come as p10 / p50 / p90 over the timed steps.
 
-The cpu_baseline leg times the fp64 oracle on (batch, head) pairs of the same prefill, and
-compares them with the timed run's output (`prefill.max_abs_err_vs_oracle`, untimed).
+The cpu_baseline leg times the fp64 oracle on whole (batch, head) pairs of the headline
+prefill and compares every row of each with the timed run's output (untimed).
 
 Prints one JSON line. Inputs are seeded synthetic tensors (synth/) resident in HBM before the
 timed region starts.
@@ -332,10 +339,12 @@ def time_decode_fp8(t, A, dwl, Dd, reps: int):
             "workload": f"{dwl.name} shapes with the cache quantized to FP8 E4M3 + fp16 per-token scales"}
 
 
-def cpu_baseline(pwl, dwl, budget_s: float, o_gpu=None):
-    """The oracle, untuned, on a time-bounded sample of the same workload. With o_gpu (the
-    timed prefill's output on the host, [B][S][Hq][D] float64) it also reports the largest
-    |GPU - oracle| over the sampled (batch, head) pairs; the comparison is not timed."""
+def cpu_baseline(pwl, budget_s: float, o_dev=None):
+    """The oracle, untuned, on a time-bounded sample of the same workload: whole (batch, head)
+    pairs, every query row of each, taken in an order that alternates batches and walks the
+    heads by 13 (so several KV heads are covered). With o_dev (the timed prefill's output, on
+    the device) every row of each sampled pair is also compared with the oracle (untimed):
+    `prefill_max_abs_err`, the largest |GPU - oracle| over them."""
     import oracle
     from synth import prefill_slab
     cores, blas = 1, "unknown"
@@ -349,24 +358,31 @@ def cpu_baseline(pwl, dwl, budget_s: float, o_gpu=None):
         pass
     G = pwl.Hq // pwl.Hkv
     pos = np.arange(pwl.S)
-    heads, flops, el, err = 0, 0.0, 0.0, 0.0
-    while heads < pwl.Hq * pwl.B and el < budget_s:
-        b, h = divmod(heads, pwl.Hq)
+    n_pairs = pwl.Hq * pwl.B
+    order = [(i % pwl.B, (i // pwl.B * 13) % pwl.Hq) for i in range(n_pairs)]
+    pairs, flops, el, err, rows = [], 0.0, 0.0, 0.0, 0
+    for b, h in order:
+        if el >= budget_s:
+            break
         q = prefill_slab(pwl, "q", b, h)
         k = prefill_slab(pwl, "k", b, h // G)
         v = prefill_slab(pwl, "v", b, h // G)
         t0 = time.perf_counter()
         ro, _ = oracle.attention_head(q, k, v, pwl.scale, pos, pwl.causal, pwl.window)
         el += time.perf_counter() - t0
-        if o_gpu is not None:
-            err = max(err, float(np.max(np.abs(o_gpu[b, :, h, :] - ro))))
-        heads += 1
+        if o_dev is not None:
+            got = o_dev[b, :, h, :].float().cpu().numpy().astype(np.float64)
+            err = max(err, float(np.max(np.abs(got - ro))))
+            rows += got.shape[0]
+        pairs.append((b, h))
         flops += 4.0 * pwl.D * prefill_pairs(pwl.S, pwl.causal, pwl.window)
     out = {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-           "sample": f"fp64 NumPy oracle prefill of {heads} of {pwl.Hq * pwl.B} (batch, head) pairs of "
-                     f"{pwl.name}, all {pwl.S} rows each, {el:.1f} s; BLAS ({blas}) threads = cores"}
-    if o_gpu is not None:
+           "sample": f"fp64 NumPy oracle prefill of {len(pairs)} of {n_pairs} (batch, head) pairs of "
+                     f"{pwl.name} ({', '.join(f'b{b}h{h}' for b, h in pairs)}), all {pwl.S} rows each, "
+                     f"{el:.1f} s; BLAS ({blas}) threads = cores"}
+    if o_dev is not None:
         out["prefill_max_abs_err"] = err  # the timed run's output, bf16, against the fp64 oracle
+        out["rows_checked"] = rows
     return out
 
 
@@ -386,16 +402,35 @@ def measured_peaks() -> dict | None:
     return json.loads(r.stdout.strip().splitlines()[-1])
 
 
+# Which calls one step runs. The first prefill workload gives `value` and `roofline`, the first
+# decode workload `roofline_decode`; every other workload gets a roofline object of its own.
+WORKLOAD_SETS = {
+    # the configurations the targets are set on (long-context sliding-window prefill; INT8 and
+    # sliding-window paged decode), with the Llama-3.2-1B-shaped prefill and decode beside them
+    "target": (["prefill_swa_s16384", "prefill_llama1b_s4096"],
+               ["decode_int8_70b_b16", "decode_swa_b32", "decode_llama1b_b64"]),
+    "llama1b": (["prefill_llama1b_s4096"], ["decode_llama1b_b64"]),
+    "swa": (["prefill_swa_s16384"], ["decode_swa_b32"]),
+    "int8_70b": ([], ["decode_int8_70b_b16"]),
+    "fp8_70b": ([], ["decode_fp8_70b_b16"]),
+}
+ROOFLINE_KEY = {  # JSON key of each workload's roofline object
+    "decode_swa_b32": "roofline_decode_swa", "decode_llama1b_b64": "roofline_decode_llama1b",
+    "prefill_llama1b_s4096": "roofline_prefill_llama1b", "prefill_swa_s16384": "roofline_prefill_swa",
+    "decode_int8_70b_b16": "roofline_decode_int8", "decode_fp8_70b_b16": "roofline_decode_fp8",
+}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llama1b", choices=["llama1b", "swa", "int8_70b", "fp8_70b"])
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0 = skip)")
+    ap.add_argument("--workload", default="target", choices=sorted(WORKLOAD_SETS))
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time (0 = skip)")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache-evicting scratch read")
     ap.add_argument("--no-chunked", action="store_true",
-                    help="skip the chunked-prefill and multi-row-decode timings reported beside the step")
+                    help="skip the chunked-prefill, multi-row, RoPE-append and FP8 timings beside the step")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured-ceiling program (MFMA loop, HBM read and gather)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -424,42 +459,50 @@ def main(argv=None):
         return 0
 
     import dataclasses
-    pwl = {"llama1b": WORKLOADS["prefill_llama1b_s4096"], "swa": WORKLOADS["prefill_swa_s16384"],
-           "int8_70b": None, "fp8_70b": None}[args.workload]
     c5 = WORKLOADS["decode_int8_70b_b16"]
-    dwl = {"llama1b": WORKLOADS["decode_llama1b_b64"], "swa": WORKLOADS["decode_swa_b32"],
-           "int8_70b": c5,
-           "fp8_70b": dataclasses.replace(c5, name="decode_fp8_70b_b16", kv_dtype="fp8")}[args.workload]
-
-    P = setup_prefill(t, pwl) if pwl else None
-    Dd = setup_decode(t, dwl)
+    wls = dict(WORKLOADS)
+    wls["decode_fp8_70b_b16"] = dataclasses.replace(c5, name="decode_fp8_70b_b16", kv_dtype="fp8")
+    pnames, dnames = WORKLOAD_SETS[args.workload]
+    pwls = [wls[n] for n in pnames]
+    dwls = [wls[n] for n in dnames]
+    print(f"bench: setting up {', '.join(pnames + dnames)}", file=sys.stderr, flush=True)
+    P = {w.name: setup_prefill(t, w) for w in pwls}
+    Dd = {w.name: setup_decode(t, w) for w in dwls}
     flush = t.ones(512 * 1024 * 1024 // 4, dtype=t.float32, device="cuda")
     t.cuda.synchronize()
 
     def step(ev=None):
         e = ev or {}
-        if "a0" in e: e["a0"].record()
-        A.kv_cache_append(Dd["kn"], Dd["vn"], Dd["seq"], Dd["pos"], Dd["table"], Dd["kc"], Dd["vc"],
-                          k_scale=Dd["ks"], v_scale=Dd["vs"])
-        if "a1" in e: e["a1"].record()
-        if not args.no_flush:
-            flush.sum()
-        if "d0" in e: e["d0"].record()
-        A.attn_decode_paged(Dd["q"], Dd["kc"], Dd["vc"], Dd["table"], Dd["ctx"], dwl.ctx_hi,
-                            k_scale=Dd["ks"], v_scale=Dd["vs"], scale=dwl.scale, window=dwl.window,
-                            out=Dd["o"], workspace=Dd["ws"])
-        if "d1" in e: e["d1"].record()
-        if P is not None:
-            if "p0" in e: e["p0"].record()
-            A.attn_prefill(P["q"], P["k"], P["v"], scale=pwl.scale, causal=pwl.causal, window=pwl.window,
-                           out=P["o"])
-            if "p1" in e: e["p1"].record()
+
+        def rec(key):
+            if key in e:
+                e[key].record()
+        for w in dwls:
+            d = Dd[w.name]
+            rec(("a0", w.name))
+            A.kv_cache_append(d["kn"], d["vn"], d["seq"], d["pos"], d["table"], d["kc"], d["vc"],
+                              k_scale=d["ks"], v_scale=d["vs"])
+            rec(("a1", w.name))
+            if not args.no_flush:
+                flush.sum()
+            rec(("d0", w.name))
+            A.attn_decode_paged(d["q"], d["kc"], d["vc"], d["table"], d["ctx"], w.ctx_hi,
+                                k_scale=d["ks"], v_scale=d["vs"], scale=w.scale, window=w.window,
+                                out=d["o"], workspace=d["ws"])
+            rec(("d1", w.name))
+        for w in pwls:
+            p = P[w.name]
+            rec(("p0", w.name))
+            A.attn_prefill(p["q"], p["k"], p["v"], scale=w.scale, causal=w.causal, window=w.window,
+                           out=p["o"])
+            rec(("p1", w.name))
 
     for _ in range(args.warmup):
         step()
     t.cuda.synchronize()
-    evs = [{n: t.cuda.Event(enable_timing=True) for n in ("a0", "a1", "d0", "d1", "p0", "p1")}
-           for _ in range(args.steps)]
+    keys = [(k, w.name) for w in dwls for k in ("a0", "a1", "d0", "d1")] + \
+           [(k, w.name) for w in pwls for k in ("p0", "p1")]
+    evs = [{k: t.cuda.Event(enable_timing=True) for k in keys} for _ in range(args.steps)]
     t.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -468,68 +511,81 @@ def main(argv=None):
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
 
-    def avg_ms(a, b):
-        return float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
+    def times(a, b):  # per-step times (ms) between two events
+        return np.array([e[a].elapsed_time(e[b]) for e in evs])
 
-    def pct_ms(a, b):  # p10 / p50 / p90 of one call over the timed steps
-        x = np.array([e[a].elapsed_time(e[b]) for e in evs])
-        return {"p10": float(np.percentile(x, 10)), "p50": float(np.percentile(x, 50)),
-                "p90": float(np.percentile(x, 90))}
-
-    d_ms = avg_ms("d0", "d1")
-    a_ms = avg_ms("a0", "a1")
-    dbytes = decode_bytes(dwl, Dd["ctx_np"])
-    d_gbs = dbytes / (d_ms * 1e-3) / 1e9
-    decode = {"kernel": "attn_decode_paged (KV split across waves + log-sum-exp merge)", "ms": d_ms, "GB/s": d_gbs,
-              "frac_hbm_peak": d_gbs / HBM_PEAK_GBS, "algorithmic_bytes": dbytes,
-              "tokens_per_s": dwl.B / (d_ms * 1e-3), "append_ms": a_ms, "ms_percentiles": pct_ms("d0", "d1"),
-              "workload": f"{dwl.name}: B={dwl.B} Hq={dwl.Hq} Hkv={dwl.Hkv} D={dwl.D} kv={dwl.kv_dtype} "
-                          f"ctx=[{dwl.ctx_lo},{dwl.ctx_hi}] window={dwl.window} block=16"}
-    roofline_decode = {"bound": "hbm", "achieved": d_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                       "frac": d_gbs / HBM_PEAK_GBS,
-                       "traffic": measured_traffic("decode", dwl.name)}
     out = {"metric": "paged decode attn HBM GB/s (% peak); prefill attn TFLOP/s (% MFMA peak)",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-           "data": "synthetic (seeded N(0,1) tensors, bf16; no dataset)"}
-    if P is not None:
-        p_ms = avg_ms("p0", "p1")
-        pfl = prefill_flops(pwl)
-        p_tf = pfl / (p_ms * 1e-3) / 1e12
-        out.update(value=p_tf, unit="TFLOP/s")
-        out["roofline"] = {"bound": "mfma", "achieved": p_tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": p_tf / BF16_PEAK_TFLOPS,
-                           "traffic": measured_traffic("prefill", pwl.name)}
-        out["prefill"] = {"kernel": "attn_prefill (bf16 MFMA)", "ms": p_ms, "TFLOP/s": p_tf,
-                          "ms_percentiles": pct_ms("p0", "p1"),
-                          "algorithmic_flops": pfl, "tokens_per_s": pwl.B * pwl.S / (p_ms * 1e-3),
-                          "workload": f"{pwl.name}: B={pwl.B} S={pwl.S} Hq={pwl.Hq} Hkv={pwl.Hkv} "
-                                      f"D={pwl.D} causal window={pwl.window}"}
+           "data": "synthetic (seeded N(0,1) tensors, bf16; INT8 cache quantized on the GPU from them; no dataset)"}
+    mfma_meas = (peaks or {}).get("mfma_bf16_tflops")
+    gather_meas = (peaks or {}).get("hbm_gather_2k_gbs")
+    decodes, prefills = {}, {}
+    for w in dwls:
+        d = Dd[w.name]
+        x = times(("d0", w.name), ("d1", w.name))
+        ms = float(x.mean())
+        byts = decode_bytes(w, d["ctx_np"])
+        gbs = byts / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("decode", w.name)}
+        if gather_meas:
+            roof["frac_of_measured"] = gbs / gather_meas  # the random 2 KB gather ceiling
+        decodes[w.name] = {
+            "kernel": "attn_decode_paged (split KV + log-sum-exp merge; time per call, both kernels)",
+            "ms": ms, "ms_percentiles": _pct(x), "GB/s": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS,
+            "algorithmic_bytes": byts, "tokens_per_s": w.B / (ms * 1e-3),
+            "append_ms": float(times(("a0", w.name), ("a1", w.name)).mean()), "roofline": roof,
+            "workload": f"{w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} kv={w.kv_dtype} "
+                        f"ctx=[{w.ctx_lo},{w.ctx_hi}] window={w.window} block=16"}
+    for w in pwls:
+        x = times(("p0", w.name), ("p1", w.name))
+        ms = float(x.mean())
+        fl = prefill_flops(w)
+        tf = fl / (ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": tf / BF16_PEAK_TFLOPS, "traffic": measured_traffic("prefill", w.name)}
+        if mfma_meas:
+            roof["frac_of_measured"] = tf / mfma_meas
+        prefills[w.name] = {
+            "kernel": "attn_prefill (bf16 MFMA)", "ms": ms, "ms_percentiles": _pct(x), "TFLOP/s": tf,
+            "algorithmic_flops": fl, "tokens_per_s": w.B * w.S / (ms * 1e-3), "roofline": roof,
+            "workload": f"{w.name}: B={w.B} S={w.S} Hq={w.Hq} Hkv={w.Hkv} D={w.D} "
+                        f"causal={w.causal} window={w.window}"}
+    if pwls:
+        head = prefills[pwls[0].name]
+        out.update(value=head["TFLOP/s"], unit="TFLOP/s")
+        out["roofline"] = head["roofline"]
     else:
-        out.update(value=d_gbs, unit="GB/s")
-        out["roofline"] = roofline_decode
-    out["decode"] = decode
-    out["roofline_decode"] = roofline_decode
+        head = decodes[dwls[0].name]
+        out.update(value=head["GB/s"], unit="GB/s")
+        out["roofline"] = head["roofline"]
+    if dwls:
+        out["roofline_decode"] = decodes[dwls[0].name]["roofline"]
+    for name, entry in list(decodes.items()) + list(prefills.items()):
+        if entry["roofline"] is not out["roofline"] and entry["roofline"] is not out.get("roofline_decode"):
+            out[ROOFLINE_KEY[name]] = entry["roofline"]
+    out["prefill"] = prefills
+    out["decode"] = decodes
     if peaks is not None:
-        # the same achieved figures against ceilings measured on this device: the bf16 MFMA
-        # loop for prefill, the random 2 KB-block gather (the paged cache's access pattern) for
-        # decode
         out["measured_peaks"] = peaks
-        if "mfma_bf16_tflops" in peaks and "roofline" in out and out["roofline"]["bound"] == "mfma":
-            out["roofline"]["frac_of_measured"] = out["roofline"]["achieved"] / peaks["mfma_bf16_tflops"]
-        if "hbm_gather_2k_gbs" in peaks:
-            roofline_decode["frac_of_measured"] = d_gbs / peaks["hbm_gather_2k_gbs"]
-    out["config"] = {"workload": (f"{pwl.name} + {dwl.name}" if pwl else dwl.name),
-                     "step": "kv_cache_append -> cache flush -> attn_decode_paged -> attn_prefill"}
-    if args.workload == "llama1b" and not args.no_chunked:
+    out["config"] = {"workload": " + ".join(pnames + dnames),
+                     "headline": {"value": pnames[0] if pnames else dnames[0],
+                                  "roofline_decode": dnames[0] if dnames else None},
+                     "step": "per decode workload: kv_cache_append -> cache flush -> attn_decode_paged; "
+                             "then attn_prefill per prefill workload"}
+    if "decode_llama1b_b64" in Dd and not args.no_chunked:
+        dwl, d3 = wls["decode_llama1b_b64"], Dd["decode_llama1b_b64"]
         out["prefill_paged"] = time_chunked(t, A, max(5, args.steps))
-        out["decode_multi"] = time_decode_multi(t, A, dwl, Dd, max(5, args.steps))
+        out["decode_multi"] = time_decode_multi(t, A, dwl, d3, max(5, args.steps))
         out["append_rope"] = time_append_rope(t, A, max(5, args.steps))
-        out["decode_fp8"] = time_decode_fp8(t, A, dwl, Dd, max(5, args.steps))
-    if args.cpu_budget > 0 and pwl is not None:
-        o_host = P["o"].float().cpu().numpy().astype(np.float64)
-        out["cpu_baseline"] = cpu_baseline(pwl, dwl, args.cpu_budget, o_host)
-        out["prefill"]["max_abs_err_vs_oracle"] = out["cpu_baseline"]["prefill_max_abs_err"]
+        out["decode_fp8"] = time_decode_fp8(t, A, dwl, d3, max(5, args.steps))
+    if args.cpu_budget > 0 and pwls:
+        w = pwls[0]
+        o_host = P[w.name]["o"]
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, o_host)
+        prefills[w.name]["max_abs_err_vs_oracle"] = out["cpu_baseline"]["prefill_max_abs_err"]
+        prefills[w.name]["rows_checked_vs_oracle"] = out["cpu_baseline"]["rows_checked"]
     print(json.dumps(out), flush=True)
     return 0
 

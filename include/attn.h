@@ -104,7 +104,10 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, float* ls
  *  max_q_len    : host-side bound on every q_len_b, used to size the grid.
  *  Requirements: D in {64, 128}; block_size == 16; Hq % Hkv == 0; total_q >= 0 (0 is a no-op);
  *  causal and window as in attn_prefill; bf16 only. Rows whose chunk is longer than the context
- *  are left unwritten; table entries outside [0, num_blocks) are never dereferenced. Cache
+ *  are left unwritten. A live table entry outside [0, num_blocks) is a caller error: it is never
+ *  dereferenced (physical block 0 is read in its place, so no access leaves the pools), and
+ *  the rows that see its keys get an unspecified result (attn_decode_paged skips such keys
+ *  instead; both give a meaningless result for a broken table). Cache
  *  slots that hold no key visible to any row of the chunk (past the context, or left of every
  *  row's window) may hold anything, NaN included, and the table entries of blocks made only
  *  of such slots may hold anything: that content never reaches the result.
@@ -128,7 +131,13 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_context
  * [TI] "分页KV缓存：借鉴操作系统的内存管理" (block table), "技术架构与模块设计" (incremental
  * decode against the cache), "推测性解码与INT8量化" (INT8 cache); sliding window: [IL].
  *
- *  q, o         : [B][Hq][D] bf16. Query b sits at position context_lens[b] - 1.
+ *  q, o         : [B][Hq][D] bf16. Query b sits at position context_lens[b] - 1. Any finite
+ *                 bf16 query is accepted: with an INT8 or FP8 cache the products run on fp16,
+ *                 and each query vector is first multiplied by a power of two that brings its
+ *                 largest element into [256, 512) (exact), the factor being taken out of the
+ *                 score again, so magnitudes beyond fp16's range (>= 65520) or below its
+ *                 subnormals lose nothing that the bf16 value holds within 2^-22 of that largest
+ *                 element.
  *  k_cache,
  *  v_cache      : [num_blocks][Hkv][block_size][D], bf16 (kv_dtype ATTN_BF16), int8 codes
  *                 (ATTN_I8) or FP8 E4M3 codes (ATTN_FP8; [TF] "3.3 FP8量化支持").

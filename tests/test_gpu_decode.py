@@ -295,3 +295,45 @@ def test_decode_int8_70b_b16_sampled():
     assert np.array_equal(vs[probe].cpu().numpy().view(np.uint16), vsc.view(np.uint16))
     for b, ro in _oracle_sampled(wl, qf, table, ctx, [0, 9], quantized):
         assert maxabs(o[b], ro) <= BF16_TOL
+
+
+@pytest.mark.parametrize("kv", ["i8", "fp8"])
+@pytest.mark.parametrize("D,window", [(64, 0), (128, 0), (128, 40)])
+def test_byte_cache_query_range(kv, D, window):
+    """Byte caches multiply on fp16: bf16 queries outside fp16's range (|q| >= 65520, or below its
+    smallest subnormal) must still match the oracle. Heads take N(0,1) queries times 3e4
+    (elements past 65504), 1e-30 and 1e-7 (below fp16's subnormals), 1, and one head mixes
+    3e4 with 1e-30 inside the same vector."""
+    import attention_attn_prefill_amd as A
+    from synth import fp8_pool
+    wl, ctx, table, nb, _, _ = _small(D, 8, 2, window, kv=kv)
+    qf = decode_query(wl)[1].astype(np.float32)
+    factors = np.array([3e4, 1e-30, 1e-7, 1.0, 3e4, 1.0, 1e-7, 1e-30], np.float32)
+    qf = qf * factors[None, :, None]
+    qf[:, 5, : D // 2] *= np.float32(3e4)
+    qf[:, 5, D // 2:] *= np.float32(1e-30)
+    from synth import bf16_bits
+    qbits = bf16_bits(qf)
+    qv = bf16_value(qbits).astype(np.float64)
+    assert np.abs(qv).max() > 65520 and 0 < np.abs(qv[:, 1]).max() < 2.0 ** -24
+    if kv == "i8":
+        kc, ks = int8_pool(wl, "k", nb)
+        vc, vs = int8_pool(wl, "v", nb)
+        kf, vf = oracle.dequantize_int8(kc, ks), oracle.dequantize_int8(vc, vs)
+    else:
+        kc, ks = fp8_pool(wl, "k", nb)
+        vc, vs = fp8_pool(wl, "v", nb)
+        kf, vf = oracle.dequantize_fp8(kc, ks), oracle.dequantize_fp8(vc, vs)
+    o = _decode(dev_bf16(qbits), dev(kc), dev(vc), dev(table), dev(ctx), wl, int(ctx.max()),
+                ks=dev(ks), vs=dev(vs))
+    ro, _ = oracle.decode_paged(qv, kf, vf, table, ctx, wl.scale, 16, window)
+    assert maxabs(host_f64(o), ro) <= BF16_TOL
+    # the same columns as draft rows of the multi-row decode (2 rows x 4 heads per KV head)
+    q2 = qbits.reshape(len(ctx), 2, 4, D)
+    om = A.attn_decode_paged_multi(dev_bf16(q2), dev(kc), dev(vc), dev(table), dev(ctx), int(ctx.max()),
+                                   k_scale=dev(ks), v_scale=dev(vs), scale=wl.scale, window=window)
+    torch().cuda.synchronize()
+    cu = np.arange(len(ctx) + 1) * 2
+    rm, _ = oracle.prefill_paged(qv.reshape(len(ctx) * 2, 4, D), cu, kf, vf, table, ctx, wl.scale, 16,
+                                 True, window)
+    assert maxabs(host_f64(om).reshape(len(ctx) * 2, 4, D), rm) <= BF16_TOL

@@ -97,20 +97,23 @@ def test_prefill_deterministic():
     assert np.array_equal(host_bits(a), host_bits(b))
 
 
-def _sampled_check(wl, rows, heads):
+def _sampled_check(wl, rows, heads, full_pairs=()):
+    """Rows `rows` of heads `heads` in every batch, and every row of the (batch, head) pairs
+    `full_pairs`, against the oracle (O and LSE)."""
     x = prefill_inputs(wl)
     o, L = _run(wl, x)
     got, gl = host_f64(o), host_f64(L)
     G = wl.Hq // wl.Hkv
     worst = 0.0
-    for b in range(wl.B):
-        for h in heads:
-            q = prefill_slab(wl, "q", b, h)[rows]
-            k = prefill_slab(wl, "k", b, h // G)
-            v = prefill_slab(wl, "v", b, h // G)
-            ro, rl = oracle.attention_head(q, k, v, wl.scale, rows, wl.causal, wl.window)
-            worst = max(worst, maxabs(got[b, rows, h], ro))
-            assert maxabs(gl[b, h, rows], rl) <= LSE_TOL_BF16
+    checks = [(b, h, rows) for b in range(wl.B) for h in heads]
+    checks += [(b, h, list(range(wl.S))) for b, h in full_pairs]
+    for b, h, rr in checks:
+        q = prefill_slab(wl, "q", b, h)[rr]
+        k = prefill_slab(wl, "k", b, h // G)
+        v = prefill_slab(wl, "v", b, h // G)
+        ro, rl = oracle.attention_head(q, k, v, wl.scale, rr, wl.causal, wl.window)
+        worst = max(worst, maxabs(got[b, rr, h], ro))
+        assert maxabs(gl[b, h, rr], rl) <= LSE_TOL_BF16
     assert worst <= BF16_TOL, worst
     return o
 
@@ -118,10 +121,13 @@ def _sampled_check(wl, rows, heads):
 def test_prefill_llama1b_s4096_sampled():
     wl = WORKLOADS["prefill_llama1b_s4096"]
     rows = [0, 1, 2, 31, 32, 63, 64, 127, 128, 129, 1000, 2047, 2048, 3071, 4094, 4095]
-    _sampled_check(wl, rows, [0, 3, 4, 17, 31])
+    _sampled_check(wl, rows, [0, 3, 4, 17, 31], full_pairs=[(0, 9), (0, 26)])
 
 
 def test_prefill_swa_s16384_sampled():
+    """The long-context sliding-window prefill at full size: sampled rows (first / last rows,
+    tile and window edges) of three heads per batch, and every one of the 16384 rows of one
+    (batch, head) pair per batch, on different KV heads."""
     wl = WORKLOADS["prefill_swa_s16384"]
     rows = [0, 1, 63, 64, 4094, 4095, 4096, 4097, 8191, 12000, 16383]
-    _sampled_check(wl, rows, [0, 5, 30])
+    _sampled_check(wl, rows, [0, 5, 30], full_pairs=[(0, 5), (1, 22)])
