@@ -41,15 +41,18 @@ typedef __attribute__((address_space(3))) void lds_void;
 // lds_off + 16 * lane. Written as asm so the compiler does not treat every later LDS read as
 // a possible alias of the in-flight copy (it would wait for the copy before unrelated LDS
 // reads); the caller awaits completion explicitly (vmcnt) before reading the data. The
-// instruction writes no registers.
+// instruction writes no registers. An LDS DMA that follows a scalar write of M0 needs one
+// wait state on this chip family (the compiler puts an s_nop there in its own code, but it
+// does not look inside asm): without it the copy can take the previous M0 and land at
+// another LDS address.
 __device__ __forceinline__ void lds_dma_16(const void* g, uint32_t lds_off) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_off), "v"(g)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_off), "v"(g)
                : "memory", "m0");
 }
 
 // As lds_dma_16 with one dword per lane: LDS byte address lds_off + 4 * lane.
 __device__ __forceinline__ void lds_dma_4(const void* g, uint32_t lds_off) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_off), "v"(g)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_off), "v"(g)
                : "memory", "m0");
 }
 

@@ -1162,7 +1162,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
     if (more) {
       if (++g == Hkv) {  // next sequence with visible blocks (one exists: pend < T)
         g = 0;
-        do ++b; while (s_pre[b + 1] == s_pre[b]);
+        do ++b; while (b < B - 1 && s_pre[b + 1] == s_pre[b]);
         nv = s_pre[b + 1] - s_pre[b];
         ctx = decode_ctx(ctx_lens, b, max_ctx, max_blocks, BS);
       }
