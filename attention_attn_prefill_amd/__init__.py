@@ -259,7 +259,7 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, max_contex
         out = torch.empty_like(q)
     need = attn_decode_workspace_size(B, Hq, Hkv, D, max_context_len, window, split_tokens)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().attn_decode_paged(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
@@ -290,7 +290,7 @@ def attn_decode_paged_multi(q, k_cache, v_cache, block_table, context_lens, max_
         out = torch.empty_like(q)
     need = attn_decode_multi_workspace_size(B, QL, Hq, Hkv, D, max_context_len, window, split_tokens)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().attn_decode_paged_multi(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),

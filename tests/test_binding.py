@@ -136,3 +136,34 @@ def test_rope_inplace_rejects():
         A.attn_rope_inplace(z(4, 2, 64), z(4, dtype=i32))
     with pytest.raises(ValueError, match="pos: dtype"):
         A.attn_rope_inplace(z(4, 2, 64), z(4, dtype=i64))
+
+
+@pytest.mark.parametrize("multi", [False, True])
+def test_auto_workspace_is_allocated_on_the_call_device(monkeypatch, multi):
+    """When no workspace is given, the binding allocates it on q's device (a host buffer passed
+    as the device workspace makes the kernel write to a host address). Host tensors stand in
+    for device ones: the device check and the library call are replaced by recorders."""
+    calls = []
+    real_empty = torch.empty
+
+    def empty(*a, **kw):
+        calls.append(kw.get("device"))
+        kw.pop("device", None)
+        return real_empty(*a, **kw)
+
+    class FakeLib:
+        def __getattr__(self, name):
+            if name.endswith("workspace_size"):
+                return lambda *a: 4096
+            return lambda *a: A.ATTN_OK
+
+    monkeypatch.setattr(A, "_on_device", lambda **kw: None)
+    monkeypatch.setattr(A, "_stream", lambda t: None)
+    monkeypatch.setattr(A, "lib", lambda: FakeLib())
+    monkeypatch.setattr(torch, "empty", empty)
+    q = z(2, 3, 8, 64) if multi else z(2, 8, 64)
+    kw = _decode_kw(q=q)
+    fn = A.attn_decode_paged_multi if multi else A.attn_decode_paged
+    fn(kw["q"], kw["k_cache"], kw["v_cache"], kw["block_table"], kw["context_lens"], 40,
+       out=torch.zeros(q.shape, dtype=bf))
+    assert calls == [q.device], calls  # the workspace, on q's device
