@@ -247,10 +247,8 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, max_contex
 
     q [B][Hq][D] bf16; caches [num_blocks][Hkv][block_size][D] bf16, int8, or uint8 /
     float8_e4m3fn holding FP8 E4M3 codes (+ fp16 scales [num_blocks][Hkv][block_size]);
-    block_table int32 [B][max_blocks]; context_lens int32 [B]. A zeroed workspace of
-    attn_decode_workspace_size(...) bytes is allocated when not given; a workspace that is
-    passed in must have been zeroed before its first use (every call leaves its counters at
-    zero again), and two calls in flight at once must not share it.
+    block_table int32 [B][max_blocks]; context_lens int32 [B]. A workspace of
+    attn_decode_workspace_size(...) bytes is allocated when not given.
     """
     import torch
     _decode_args(q, k_cache, v_cache, block_table, context_lens, k_scale, v_scale, out, workspace,
@@ -260,8 +258,8 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, max_contex
     if out is None:
         out = torch.empty_like(q)
     need = attn_decode_workspace_size(B, Hq, Hkv, D, max_context_len, window, split_tokens)
-    if workspace is None and need > 0:  # zeroed: the counters at its start must begin at 0
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().attn_decode_paged(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
@@ -291,8 +289,8 @@ def attn_decode_paged_multi(q, k_cache, v_cache, block_table, context_lens, max_
     if out is None:
         out = torch.empty_like(q)
     need = attn_decode_multi_workspace_size(B, QL, Hq, Hkv, D, max_context_len, window, split_tokens)
-    if workspace is None and need > 0:  # zeroed: the counters at its start must begin at 0
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().attn_decode_paged_multi(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),

@@ -972,67 +972,6 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
                     out + ((int64_t)row * Hq + h) * D);
 }
 
-// Log-sum-exp merge of the n partials of one (sequence, KV head) segment, slots
-// slot0 .. slot0 + n - 1 of ncol columns each, by one wave with every column at once: lane l
-// takes column l / (64 / GP) and DPL = D * GP / 64 consecutive d. Per element the arithmetic
-// and the order of the partials are those of merge_partials (a running max that moves as
-// partials arrive), so the result is the same bit for bit whichever wave merges.
-template <int D, int GP>
-__device__ __forceinline__ void merge_segment(const float* __restrict__ part_o,
-                                              const float* __restrict__ part_lse, int64_t slot0,
-                                              int n, int ncol, uint16_t* __restrict__ out, int b,
-                                              int g, int G, int QL, int Hq) {
-  constexpr int LPC = 64 / GP, DPL = D / LPC;
-  constexpr int BATCH = DPL >= 32 ? 2 : 4;  // partials whose loads are in flight together
-  const int lane = threadIdx.x & 63;
-  const int h = lane / LPC, d0 = (lane % LPC) * DPL;
-  const bool live = h < ncol;
-  const int hh = live ? h : 0;  // idle lanes read column 0 and write nothing
-  float M = -INFINITY, L = 0.f, acc[DPL];
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
-  for (int i = 0; i < n; i += BATCH) {
-    float ls[BATCH], ov[BATCH][DPL];
-#pragma unroll
-    for (int k = 0; k < BATCH; ++k) {
-      const bool ok = i + k < n;
-      const int64_t idx = (slot0 + i + k) * ncol + hh;
-      ls[k] = ok ? part_lse[idx] : -INFINITY;
-      const float* src = part_o + idx * D + d0;
-      if constexpr (DPL % 4 == 0) {
-#pragma unroll
-        for (int e = 0; e < DPL; e += 4) {
-          const f32x4 x = ok ? *reinterpret_cast<const f32x4*>(src + e) : (f32x4){0.f, 0.f, 0.f, 0.f};
-          ov[k][e] = x[0]; ov[k][e + 1] = x[1]; ov[k][e + 2] = x[2]; ov[k][e + 3] = x[3];
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) ov[k][e] = ok ? src[e] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < BATCH; ++k) {
-      if (ls[k] == -INFINITY) continue;
-      if (ls[k] > M) {
-        const float r = fast_exp2(M - ls[k]);  // M = -inf at first: r = 0
-        L *= r;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[e] *= r;
-        M = ls[k];
-      }
-      const float w = fast_exp2(ls[k] - M);
-      L += w;
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[e] = fmaf(w, ov[k][e], acc[e]);
-    }
-  }
-  if (!live) return;
-  const float inv = L > 0.f ? 1.0f / L : 0.f;
-  uint16_t* orow = out + (((int64_t)b * QL + h / G) * Hq + g * G + h % G) * D + d0;
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) orow[e] = (uint16_t)f32_to_bf16_bits(acc[e] * inv);
-}
-
 // ---- balanced: persistent waves over equal ranges of the (b, g, block) list -----------------
 // Sequence b contributes nvis(b) blocks per KV head (the blocks holding positions
 // [lo_b, ctx_b)); the list orders blocks by (b, g, block). With T = Hkv * sum nvis and P waves,
@@ -1053,7 +992,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
     const void* __restrict__ v_cache, const __half* __restrict__ k_scale,
     const __half* __restrict__ v_scale, const int32_t* __restrict__ table,
     const int32_t* __restrict__ ctx_lens, uint16_t* __restrict__ out,
-    int32_t* __restrict__ seg_cnt, float* __restrict__ part_o, float* __restrict__ part_lse,
+    int32_t* __restrict__ prefix_out, float* __restrict__ part_o, float* __restrict__ part_lse,
     int B, int Hq, int Hkv, int G, int QL, int max_blocks, int num_blocks, int max_ctx,
     float scale_log2) {
   using W = DecodeWaveT<D, GP, KV>;
@@ -1066,8 +1005,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // ---- prefix of visible blocks over the sequences (every workgroup): per-thread runs, a
-  // scan inside each wave, then the wave totals
+  // ---- prefix of visible blocks over the sequences (every workgroup; workgroup 0 also
+  // stores it for the merge): per-thread runs, a scan inside each wave, then the wave totals
   {
     const int per = (B + kDecodeThreads - 1) / kDecodeThreads;
     const int b0 = tid * per;
@@ -1091,14 +1030,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
     }
     if (tid == kDecodeThreads - 1) s_pre[B] = base + incl;
     __syncthreads();
-    // sequences with no visible block (empty context) are in no wave's range: workgroup 0
-    // writes their zeros
     if (blockIdx.x == 0)
-      for (int bb = tid; bb < B; bb += kDecodeThreads)
-        if (s_pre[bb + 1] == s_pre[bb]) {
-          u32x4* dst = reinterpret_cast<u32x4*>(out + (int64_t)bb * QL * Hq * D);
-          for (int i = 0; i < QL * Hq * D / 8; ++i) dst[i] = (u32x4){0u, 0u, 0u, 0u};
-        }
+      for (int i = tid; i <= B; i += kDecodeThreads) prefix_out[i] = s_pre[i];
   }
 
   const int64_t T = (int64_t)Hkv * s_pre[B];
@@ -1225,8 +1158,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
     // ---- the next piece's Q and first chunk are issued before this one is written out -----
     const int ob = b, og = g;
     const bool whole = j0 == 0 && j1 == nv;
-    const int64_t oseg0 = seg0;  // list position of the segment's first block
-    const int onv = nv;
     const bool more = pend < end;
     if (more) {
       if (++g == Hkv) {  // next sequence with visible blocks (one exists: pend < T)
@@ -1285,28 +1216,39 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
         if (d0 == 0) part_lse[slot * ncol + h] = lh > 0.f ? mh + __log2f(lh) : -INFINITY;
       }
     });
-    if (!whole) {
-      // The segment's pieces sit in waves p0 .. p1. Its counter is indexed by p0: the list
-      // position (p0 + 1) * qn lies strictly inside this segment, and inside no other, so
-      // the index is unique among segments with more than one piece (and < P). The wave
-      // whose piece arrives last merges all of them and leaves the counter at zero again.
-      const int64_t p0 = oseg0 / qn, p1 = (oseg0 + onv - 1) / qn;
-      const int npiece = (int)(p1 - p0 + 1);
-      __threadfence();  // release: this wave's partial is visible device-wide (across XCDs)
-      int last = 0;
-      if (lane == 0)
-        last = __hip_atomic_fetch_add(seg_cnt + p0, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
-               npiece - 1;
-      if (__builtin_amdgcn_readfirstlane(last)) {
-        __threadfence();  // acquire: the other pieces' partials
-        merge_segment<D, GP>(part_o, part_lse, (int64_t)ob * Hkv + og + p0, npiece, ncol, out, ob, og,
-                             G, QL, Hq);
-        if (lane == 0) __hip_atomic_store(seg_cnt + p0, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
     if (!more) break;
     w.reset();
   }
+}
+
+// Merge for the balanced shape: column hl of KV head g of sequence b gathers the pieces of
+// segment s = (b, g) from slots s + p0 .. s + p1; a segment held by one wave was written
+// directly. One wave per column and kMergeCols columns per workgroup: an eighth of the
+// workgroups that one column each would need (C3 -0.6 us, measured).
+constexpr int kMergeCols = 8;
+template <int D>
+__global__ __launch_bounds__(64 * kMergeCols) void decode_stream_merge_kernel(
+    const int32_t* __restrict__ prefix, const float* __restrict__ part_o,
+    const float* __restrict__ part_lse, uint16_t* __restrict__ out, int B, int Hq, int Hkv,
+    int G, int QL, int P) {
+  const int ncol = G * QL;
+  const int c = blockIdx.x * kMergeCols + (threadIdx.x >> 6);  // one column per wave
+  if (c >= Hkv * ncol) return;
+  const int g = c / ncol, hl = c % ncol, b = blockIdx.y;  // column hl of g
+  const int nv = prefix[b + 1] - prefix[b];
+  uint16_t* orow = out + (((int64_t)b * QL + hl / G) * Hq + g * G + hl % G) * D;
+  if (nv == 0) {  // empty context: zeros
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) orow[(threadIdx.x & 63) + 64 * e] = 0;
+    return;
+  }
+  const int64_t T = (int64_t)Hkv * prefix[B];
+  const int64_t qn = (T + P - 1) / P;
+  const int64_t seg0 = (int64_t)Hkv * prefix[b] + (int64_t)g * nv;
+  const int64_t p0 = seg0 / qn, p1 = (seg0 + nv - 1) / qn;
+  if (p0 == p1) return;
+  const int64_t s = (int64_t)b * Hkv + g;
+  merge_partials<D>(part_o, part_lse, (s + p0) * ncol + hl, ncol, (int)(p1 - p0 + 1), orow);
 }
 
 static int pow2_at_least(int g) {
@@ -1342,12 +1284,12 @@ DecodePlan plan_decode(int B, int QL, int Hq, int Hkv, int D, int max_context_le
     // ranges per wave mean fewer partials to write and merge, and the 8 waves still keep
     // enough loads in flight)
     const int64_t max_entries = (int64_t)B * Hkv * ((span + 15) / 16 + 1);
-    const int64_t waves = std::min<int64_t>(std::min<int64_t>((int64_t)device_cus() * 8, max_entries),
-                                            kDecodeCounters);
+    const int64_t waves = std::min<int64_t>((int64_t)device_cus() * 8, max_entries);
     p.stream = true;
     p.stream_waves_max = (int)std::max<int64_t>(kDecodeWaves, waves);
     const size_t slots = (size_t)B * Hkv + p.stream_waves_max;
-    p.part_o_off = kDecodeCounterBytes;  // the arrival counters come first, in every layout
+    p.prefix_off = 0;
+    p.part_o_off = align256((size_t)(B + 1) * sizeof(int32_t));
     p.part_lse_off = p.part_o_off + align256(slots * ncol * D * sizeof(float));
     p.workspace_bytes = p.part_lse_off + slots * ncol * sizeof(float);
     return p;
@@ -1368,8 +1310,8 @@ DecodePlan plan_decode(int B, int QL, int Hq, int Hkv, int D, int max_context_le
     p.workspace_bytes = 0;
   } else {
     const size_t parts = (size_t)B * Hkv * ncol * p.n_split;
-    p.part_o_off = kDecodeCounterBytes;  // left untouched, so a shared workspace keeps them
-    p.part_lse_off = p.part_o_off + align256(parts * D * sizeof(float));
+    p.part_o_off = 0;
+    p.part_lse_off = align256(parts * D * sizeof(float));
     p.workspace_bytes = p.part_lse_off + parts * sizeof(float);
   }
   return p;
@@ -1384,15 +1326,19 @@ static void launch_stream(const DecodeArgs& a, hipStream_t stream) {
     per_cu = 1;
   const int wgs = std::max(1, std::min(device_cus() * per_cu, a.plan.stream_waves_max / kDecodeWaves));
   char* ws = reinterpret_cast<char*>(a.workspace);
-  int32_t* seg_cnt = reinterpret_cast<int32_t*>(ws);
+  int32_t* prefix = reinterpret_cast<int32_t*>(ws + a.plan.prefix_off);
   float* part_o = reinterpret_cast<float*>(ws + a.plan.part_o_off);
   float* part_lse = reinterpret_cast<float*>(ws + a.plan.part_lse_off);
   const int G = a.Hq / a.Hkv;
   hipLaunchKernelGGL(kern, dim3(wgs), dim3(kDecodeThreads), 0, stream, (const uint16_t*)a.q,
                      a.k_cache, a.v_cache, (const __half*)a.k_scale, (const __half*)a.v_scale,
-                     a.block_table, a.context_lens, (uint16_t*)a.o, seg_cnt, part_o, part_lse, a.B,
+                     a.block_table, a.context_lens, (uint16_t*)a.o, prefix, part_o, part_lse, a.B,
                      a.Hq, a.Hkv, G, a.q_len, a.max_blocks_per_seq, a.num_blocks,
                      a.max_context_len, a.scale * kLog2e);
+  const int merge_wgs = (a.Hkv * G * a.q_len + kMergeCols - 1) / kMergeCols;
+  hipLaunchKernelGGL(decode_stream_merge_kernel<D>, dim3(merge_wgs, a.B), dim3(64 * kMergeCols), 0,
+                     stream, prefix, part_o, part_lse, (uint16_t*)a.o, a.B, a.Hq, a.Hkv, G,
+                     a.q_len, wgs * kDecodeWaves);
 }
 
 template <int D, int GP, int KV>

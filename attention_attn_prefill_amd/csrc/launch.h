@@ -25,19 +25,13 @@ constexpr int kKvBf16 = 0, kKvI8 = 1, kKvFp8 = 2;
 constexpr int kMaxSplitTokens = 8192;  // largest split_tokens a decode call accepts
 constexpr int kStreamMaxB = 2048;      // largest batch of the balanced decode shape
 constexpr int kMaxDevices = 64;        // devices with per-device launch state (attributes set once)
-// Decode workspaces begin with kDecodeCounters int32 arrival counters (the balanced shape's
-// in-kernel merge); they must be zero when a workspace is first used, and every call leaves
-// them zero. Every workspace layout keeps them at offset 0.
-constexpr int kDecodeCounters = 8192;
-constexpr size_t kDecodeCounterBytes = kDecodeCounters * sizeof(int32_t);
-static_assert(kDecodeCounterBytes == 32768, "the workspace contract in attn.h names 32768 bytes");
 
 struct DecodePlan {
   bool stream;           // balanced persistent shape (else fixed splits)
   int stream_waves_max;  // balanced: most waves a launch may use (sizes the partial slots)
   int split_tokens;      // fixed split: tokens per workgroup along the KV axis (multiple of 16)
   int n_split;           // fixed split: workgroups per (sequence, KV head)
-  size_t part_o_off, part_lse_off;  // workspace layout (bytes; counters at offset 0)
+  size_t prefix_off, part_o_off, part_lse_off;  // workspace layout (bytes)
   size_t workspace_bytes;
 };
 

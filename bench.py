@@ -156,7 +156,7 @@ def setup_decode(t, wl):
     d["pos"] = (d["ctx"] - 1).to(t.int32)
     d["o"] = t.empty_like(d["q"])
     need = A.attn_decode_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.D, wl.ctx_hi, wl.window, 0)
-    d["ws"] = t.zeros(max(need, 1), dtype=t.uint8, device="cuda")  # counters start at zero
+    d["ws"] = t.empty(max(need, 1), dtype=t.uint8, device="cuda")
     return d
 
 
@@ -231,7 +231,7 @@ def time_decode_multi(t, A, dwl, Dd, reps: int, q_len: int = 4):
     q = _bf16(t, qb).view(dwl.B, q_len, dwl.Hq, dwl.D)
     o = t.empty_like(q)
     need = A.attn_decode_multi_workspace_size(dwl.B, q_len, dwl.Hq, dwl.Hkv, dwl.D, dwl.ctx_hi, dwl.window, 0)
-    ws = t.zeros(max(need, 1), dtype=t.uint8, device="cuda")  # counters start at zero
+    ws = t.empty(max(need, 1), dtype=t.uint8, device="cuda")
     flush = t.ones(512 * 1024 * 1024 // 4, dtype=t.float32, device="cuda")
 
     def call():
@@ -466,13 +466,8 @@ def main(argv=None):
     pwls = [wls[n] for n in pnames]
     dwls = [wls[n] for n in dnames]
     print(f"bench: setting up {', '.join(pnames + dnames)}", file=sys.stderr, flush=True)
-    P, Dd = {}, {}
-    for w in pwls:
-        P[w.name] = setup_prefill(t, w)
-        print(f"bench: {w.name} ready", file=sys.stderr, flush=True)
-    for w in dwls:
-        Dd[w.name] = setup_decode(t, w)
-        print(f"bench: {w.name} ready", file=sys.stderr, flush=True)
+    P = {w.name: setup_prefill(t, w) for w in pwls}
+    Dd = {w.name: setup_decode(t, w) for w in dwls}
     flush = t.ones(512 * 1024 * 1024 // 4, dtype=t.float32, device="cuda")
     t.cuda.synchronize()
 

@@ -165,12 +165,8 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_context
  *                 (ATTN_ERR_UNSUPPORTED above): fixed splits of that many tokens.
  *                 Results are run-to-run identical for a given split_tokens on a given GPU.
  *  workspace    : device buffer of at least attn_decode_workspace_size(...) bytes (may be NULL
- *                 when that size is 0). Its first 32768 bytes are arrival counters of the
- *                 balanced shape's in-kernel merge: they must be zero before the workspace is
- *                 first used (allocate it zeroed), and every call leaves them zero again, so a
- *                 workspace can be reused by any later call (any shape, single- or multi-row)
- *                 as long as nothing else writes it. The rest is scratch, overwritten by the
- *                 call. Two calls in flight at once must not share a workspace.
+ *                 when that size is 0); overwritten by the call; its contents on entry do not
+ *                 matter. Two calls in flight at once must not share a workspace.
  *  Requirements: D in {64, 128}; block_size == 16; Hq % Hkv == 0 and Hq / Hkv <= 16;
  *                 q, o, k_cache, v_cache, k_scale and v_scale 16-byte aligned (else
  *                 ATTN_ERR_SHAPE).

@@ -140,16 +140,16 @@ def test_rope_inplace_rejects():
 
 @pytest.mark.parametrize("multi", [False, True])
 def test_auto_workspace_is_allocated_on_the_call_device(monkeypatch, multi):
-    """When no workspace is given, the binding allocates it zeroed on q's device (a host buffer
-    passed as the device workspace makes the kernel write to a host address). Host tensors stand in
+    """When no workspace is given, the binding allocates it on q's device (a host buffer passed
+    as the device workspace makes the kernel write to a host address). Host tensors stand in
     for device ones: the device check and the library call are replaced by recorders."""
     calls = []
-    real_zeros = torch.zeros
+    real_empty = torch.empty
 
-    def zeros(*a, **kw):
+    def empty(*a, **kw):
         calls.append(kw.get("device"))
         kw.pop("device", None)
-        return real_zeros(*a, **kw)
+        return real_empty(*a, **kw)
 
     class FakeLib:
         def __getattr__(self, name):
@@ -160,10 +160,10 @@ def test_auto_workspace_is_allocated_on_the_call_device(monkeypatch, multi):
     monkeypatch.setattr(A, "_on_device", lambda **kw: None)
     monkeypatch.setattr(A, "_stream", lambda t: None)
     monkeypatch.setattr(A, "lib", lambda: FakeLib())
+    monkeypatch.setattr(torch, "empty", empty)
     q = z(2, 3, 8, 64) if multi else z(2, 8, 64)
     kw = _decode_kw(q=q)
-    out = torch.zeros(q.shape, dtype=bf)
-    monkeypatch.setattr(torch, "zeros", zeros)
     fn = A.attn_decode_paged_multi if multi else A.attn_decode_paged
-    fn(kw["q"], kw["k_cache"], kw["v_cache"], kw["block_table"], kw["context_lens"], 40, out=out)
-    assert calls == [q.device], calls  # the workspace, zeroed, on q's device
+    fn(kw["q"], kw["k_cache"], kw["v_cache"], kw["block_table"], kw["context_lens"], 40,
+       out=torch.zeros(q.shape, dtype=bf))
+    assert calls == [q.device], calls  # the workspace, on q's device

@@ -306,7 +306,7 @@ def test_byte_cache_query_range(kv, D, window):
     3e4 with 1e-30 inside the same vector."""
     import attention_attn_prefill_amd as A
     from synth import fp8_pool
-    wl, ctx, table, nb, _, _ = _small(D, 8, 2, window, kv=kv, ctx=(2, 15, 16, 17, 100, 333))
+    wl, ctx, table, nb, _, _ = _small(D, 8, 2, window, kv=kv)
     qf = decode_query(wl)[1].astype(np.float32)
     factors = np.array([3e4, 1e-30, 1e-7, 1.0, 3e4, 1.0, 1e-7, 1e-30], np.float32)
     qf = qf * factors[None, :, None]
@@ -339,11 +339,10 @@ def test_byte_cache_query_range(kv, D, window):
     assert maxabs(host_f64(om).reshape(len(ctx) * 2, 4, D), rm) <= BF16_TOL
 
 
-def test_shared_workspace_bit_identical_and_counters_left_zero():
-    """One zeroed workspace reused by calls of different shapes (balanced single-row, multi-row,
-    fixed splits with and without a window, the balanced call again) gives the same bits as a fresh
-    workspace per call, and its arrival counters (the first 32768 bytes) are zero after every
-    call."""
+def test_shared_workspace_bit_identical():
+    """One workspace reused by calls of different shapes (balanced single-row, multi-row, fixed
+    splits with and without a window, the balanced call again) gives the same bits as a fresh
+    workspace per call: nothing a call leaves in the workspace reaches a later call."""
     import attention_attn_prefill_amd as A
     t = torch()
     wl, ctx, table, nb, qbits, qf = _small(64, 8, 2, 0, ctx=(1, 15, 16, 17, 100, 333, 2000, 40))
@@ -353,7 +352,7 @@ def test_shared_workspace_bit_identical_and_counters_left_zero():
     q2 = dev_bf16(np.concatenate([qbits, qbits[:, ::-1]], axis=1).reshape(len(ctx), 2, 8, 64))
     need = max(A.attn_decode_workspace_size(len(ctx), 8, 2, 64, mx, w, sp) for w, sp in ((0, 0), (0, 32), (300, 64)))
     need = max(need, A.attn_decode_multi_workspace_size(len(ctx), 2, 8, 2, 64, mx, 0, 0))
-    ws = t.zeros(need, dtype=t.uint8, device="cuda")
+    ws = t.full((need,), 0x7F, dtype=t.uint8, device="cuda")  # starts as NaN-like garbage
     calls = [
         lambda w: A.attn_decode_paged(q, kc, vc, tb, cx, mx, scale=wl.scale, workspace=w),
         lambda w: A.attn_decode_paged_multi(q2, kc, vc, tb, cx, mx, scale=wl.scale, workspace=w),
@@ -367,6 +366,5 @@ def test_shared_workspace_bit_identical_and_counters_left_zero():
         fresh = call(None)
         t.cuda.synchronize()
         assert np.array_equal(host_bits(shared), host_bits(fresh))
-        assert int(ws[:32768].view(t.int32).abs().sum().item()) == 0
     ro, _ = oracle.decode_paged(qf, bf16_value(kb), bf16_value(vb), table, ctx, wl.scale, 16)
     assert maxabs(host_f64(calls[0](ws)), ro) <= BF16_TOL
