@@ -3,8 +3,8 @@
 Every computation runs in the HIP kernels of libattn.so; torch supplies device memory and the
 current stream. The names follow the C ABI in include/attn.h: attn_prefill,
 attn_prefill_paged, attn_decode_paged, attn_decode_paged_multi, kv_cache_append,
-attn_decode_workspace_size, attn_decode_multi_workspace_size, kv_cache_append_rope,
-attn_rope_inplace.
+attn_decode_workspace_size, attn_decode_multi_workspace_size, attn_decode_paged_noalloc,
+kv_cache_append_rope, attn_rope_inplace.
 """
 from __future__ import annotations
 
@@ -29,6 +29,8 @@ _SIGS = {
                                 _I, _I, ctypes.c_float, _I, _I, _P]),
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
                                ctypes.c_float, _I, _I, _P, ctypes.c_size_t, _P]),
+    "attn_decode_paged_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
+                                       ctypes.c_float, _I, _I, _P]),
     "attn_decode_multi_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "attn_decode_paged_multi": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
                                      _I, _I, ctypes.c_float, _I, _I, _P, ctypes.c_size_t, _P]),
@@ -267,6 +269,26 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, max_contex
         block_table.shape[1], num_blocks, int(max_context_len),
         float(D ** -0.5 if scale is None else scale), int(window), int(split_tokens),
         _ptr(workspace), ws_bytes, _stream(q)))
+    return out
+
+
+def attn_decode_paged_noalloc(q, k_cache, v_cache, block_table, context_lens, max_context_len: int, *,
+                              k_scale=None, v_scale=None, scale: float | None = None, window: int = 0,
+                              split_tokens: int = 0, out=None):
+    """attn_decode_paged without a workspace: the library keeps the partials in a static
+    per-GPU device array (32 MiB). Calls that may overlap on one GPU must not be issued."""
+    import torch
+    _decode_args(q, k_cache, v_cache, block_table, context_lens, k_scale, v_scale, out, None,
+                 False)
+    B, Hq, D = q.shape
+    num_blocks, Hkv, bs, _ = k_cache.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib().attn_decode_paged_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+        _ptr(context_lens), _ptr(out), _dtype_code(k_cache), B, Hq, Hkv, D, bs,
+        block_table.shape[1], num_blocks, int(max_context_len),
+        float(D ** -0.5 if scale is None else scale), int(window), int(split_tokens), _stream(q)))
     return out
 
 

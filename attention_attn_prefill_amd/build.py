@@ -9,7 +9,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn.so")
-SOURCES = ["attn_api.cpp", "append.hip", "decode.hip", "prefill_bf16.hip", "prefill_f32.hip"]
+SOURCES = ["attn_api.cpp", "append.hip", "decode.hip", "noalloc.hip", "prefill_bf16.hip", "prefill_f32.hip"]
 
 # Packed-fp32 VALU forms are kept out of the code objects on purpose.
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",

@@ -139,7 +139,8 @@ static int decode_impl(const char* who, const void* q, const void* k_cache, cons
                        const int32_t* context_lens, void* o, int kv_dtype, int B, int q_len,
                        int Hq, int Hkv, int D, int block_size, int max_blocks_per_seq,
                        int num_blocks, int max_context_len, float scale, int window,
-                       int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+                       int split_tokens, void* workspace, size_t workspace_bytes, void* stream,
+                       bool static_scratch = false) {
   if (!q || !k_cache || !v_cache || !block_table || !context_lens || !o)
     return fail(ATTN_ERR_NULL, "q, k_cache, v_cache, block_table, context_lens and o are required");
   if (kv_dtype != ATTN_BF16 && kv_dtype != ATTN_I8 && kv_dtype != ATTN_FP8)
@@ -168,6 +169,16 @@ static int decode_impl(const char* who, const void* q, const void* k_cache, cons
   if (B > 65535 / q_len || Hkv > 65535) return fail(ATTN_ERR_SHAPE, "B * q_len and Hkv must be <= 65535");
   attn::DecodePlan plan =
       attn::plan_decode(B, q_len, Hq, Hkv, D, max_context_len, window, split_tokens);
+  if (static_scratch) {
+    // the partials go to this GPU's static scratch array instead of a caller workspace
+    if (plan.workspace_bytes > attn::kNoAllocScratchBytes)
+      return fail(ATTN_ERR_WORKSPACE,
+                  "%s needs %zu bytes of scratch here; the static scratch holds %zu", who,
+                  plan.workspace_bytes, attn::kNoAllocScratchBytes);
+    const hipError_t e = attn::noalloc_scratch(&workspace);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s: scratch address: %s", who, hipGetErrorString(e));
+    workspace_bytes = attn::kNoAllocScratchBytes;
+  }
   if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
     return fail(ATTN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", plan.workspace_bytes,
                 workspace ? workspace_bytes : (size_t)0);
@@ -188,6 +199,18 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                      context_lens, o, kv_dtype, B, 1, Hq, Hkv, D, block_size, max_blocks_per_seq,
                      num_blocks, max_context_len, scale, window, split_tokens, workspace,
                      workspace_bytes, stream);
+}
+
+int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const void* k_scale, const void* v_scale,
+                              const int32_t* block_table, const int32_t* context_lens, void* o,
+                              int kv_dtype, int B, int Hq, int Hkv, int D, int block_size,
+                              int max_blocks_per_seq, int num_blocks, int max_context_len,
+                              float scale, int window, int split_tokens, void* stream) {
+  return decode_impl("attn_decode_paged_noalloc", q, k_cache, v_cache, k_scale, v_scale,
+                     block_table, context_lens, o, kv_dtype, B, 1, Hq, Hkv, D, block_size,
+                     max_blocks_per_seq, num_blocks, max_context_len, scale, window, split_tokens,
+                     nullptr, 0, stream, /*static_scratch=*/true);
 }
 
 int attn_decode_paged_multi(const void* q, const void* k_cache, const void* v_cache,

@@ -25,6 +25,9 @@ constexpr int kKvBf16 = 0, kKvI8 = 1, kKvFp8 = 2;
 constexpr int kMaxSplitTokens = 8192;  // largest split_tokens a decode call accepts
 constexpr int kStreamMaxB = 2048;      // largest batch of the balanced decode shape
 constexpr int kMaxDevices = 64;        // devices with per-device launch state (attributes set once)
+// Device scratch of attn_decode_paged_noalloc: one static array per GPU, held until the
+// process ends.
+constexpr size_t kNoAllocScratchBytes = 32u << 20;
 
 struct DecodePlan {
   bool stream;           // balanced persistent shape (else fixed splits)
@@ -96,6 +99,10 @@ int launch_kv_append_rope(const AppendArgs& a, double rope_base, hipStream_t str
 int launch_rope_rows(void* x, const int32_t* pos, int T, int H, int D, double rope_base,
                      hipStream_t stream);
 int launch_prefill_paged(const PrefillPagedArgs& a, hipStream_t stream);
+
+// Device address of this GPU's static decode scratch (kNoAllocScratchBytes), looked up once
+// per device with that device current.
+hipError_t noalloc_scratch(void** ptr);
 
 // Workgroups and threads per workgroup of a bf16 prefill launch over B sequences of up to S
 // query rows (the grid is one-dimensional).

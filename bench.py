@@ -466,8 +466,13 @@ def main(argv=None):
     pwls = [wls[n] for n in pnames]
     dwls = [wls[n] for n in dnames]
     print(f"bench: setting up {', '.join(pnames + dnames)}", file=sys.stderr, flush=True)
-    P = {w.name: setup_prefill(t, w) for w in pwls}
-    Dd = {w.name: setup_decode(t, w) for w in dwls}
+    P, Dd = {}, {}
+    for w in pwls:
+        P[w.name] = setup_prefill(t, w)
+        print(f"bench: {w.name} ready", file=sys.stderr, flush=True)
+    for w in dwls:
+        Dd[w.name] = setup_decode(t, w)
+        print(f"bench: {w.name} ready", file=sys.stderr, flush=True)
     flush = t.ones(512 * 1024 * 1024 // 4, dtype=t.float32, device="cuda")
     t.cuda.synchronize()
 

@@ -180,6 +180,31 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_decode_paged_noalloc -- attn_decode_paged with no workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. It computes exactly what attn_decode_paged computes with the same
+ * arguments (the same kernels; the results are bit-identical) and allocates nothing: the
+ * split-KV partials go to a static device array of 32 MiB per GPU, created with the library's
+ * code object and held until the process ends. Its address is looked up once per device
+ * (hipGetSymbolAddress, with that device current).
+ *  - A call whose partials need more than the 32 MiB returns ATTN_ERR_WORKSPACE before any
+ *    launch (attn_decode_workspace_size gives the need; e.g. the balanced shape needs about
+ *    (B*Hkv + 8*CUs) * (Hq/Hkv) * D * 4 bytes).
+ *  - Every call on one GPU shares that GPU's array and overwrites it: calls that may overlap
+ *    on one GPU (different streams without ordering between them, or threads) race, and their
+ *    results are undefined. Calls ordered on one stream are safe.
+ *  - Nothing has to be initialised: the array's contents on entry do not matter.
+ * Other arguments and status codes: as attn_decode_paged.
+ */
+int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const void* k_scale, const void* v_scale,
+                              const int32_t* block_table, const int32_t* context_lens, void* o,
+                              int kv_dtype, int B, int Hq, int Hkv, int D,
+                              int block_size, int max_blocks_per_seq, int num_blocks,
+                              int max_context_len, float scale, int window, int split_tokens,
+                              void* stream);
+
+/*
  * attn_decode_multi_workspace_size -- as attn_decode_workspace_size, for attn_decode_paged_multi
  * with q_len query rows per sequence.
  */

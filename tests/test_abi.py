@@ -208,3 +208,30 @@ def test_fp8_cache_validation():
     assert _decode(kv=4) == A.ATTN_ERR_DTYPE
     assert _append(dt=A.ATTN_FP8) == A.ATTN_ERR_NULL
     assert _append(dt=A.ATTN_FP8, T=0, kn=None) == A.ATTN_OK
+
+
+def _noalloc(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, ks=None, vs=None, table=FAKE, ctx=FAKE, o=FAKE,
+             kv=A.ATTN_BF16, B=2, Hq=8, Hkv=2, D=64, bs=16, mb=4, nb=8, maxctx=64, scale=0.125,
+             window=0, split=0)
+    a.update(kw)
+    return A.lib().attn_decode_paged_noalloc(a["q"], a["kc"], a["vc"], a["ks"], a["vs"], a["table"],
+                                             a["ctx"], a["o"], a["kv"], a["B"], a["Hq"], a["Hkv"], a["D"],
+                                             a["bs"], a["mb"], a["nb"], a["maxctx"], a["scale"],
+                                             a["window"], a["split"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), A.ATTN_ERR_NULL), (dict(kv=A.ATTN_F32), A.ATTN_ERR_DTYPE),
+    (dict(Hq=6, Hkv=4), A.ATTN_ERR_SHAPE), (dict(D=80), A.ATTN_ERR_UNSUPPORTED),
+    (dict(o=ctypes.c_void_p(0x1004)), A.ATTN_ERR_SHAPE),
+    # partials of 2048 sequences x 16 query heads per KV head x D = 128 exceed the 32 MiB array
+    (dict(B=2048, Hq=128, Hkv=8, D=128, maxctx=1000), A.ATTN_ERR_WORKSPACE),
+    (dict(B=512, Hq=64, Hkv=8, D=128, maxctx=100000, split=64), A.ATTN_ERR_WORKSPACE),
+])
+def test_noalloc_validation(kw, code):
+    """Rejected before the device is touched (no GPU here), oversized requests with a message
+    that names the static scratch's size."""
+    assert _noalloc(**kw) == code
+    if code == A.ATTN_ERR_WORKSPACE:
+        assert b"static scratch holds 33554432" in A.lib().attn_last_error()

@@ -306,7 +306,7 @@ def test_byte_cache_query_range(kv, D, window):
     3e4 with 1e-30 inside the same vector."""
     import attention_attn_prefill_amd as A
     from synth import fp8_pool
-    wl, ctx, table, nb, _, _ = _small(D, 8, 2, window, kv=kv)
+    wl, ctx, table, nb, _, _ = _small(D, 8, 2, window, kv=kv, ctx=(2, 15, 16, 17, 100, 333))
     qf = decode_query(wl)[1].astype(np.float32)
     factors = np.array([3e4, 1e-30, 1e-7, 1.0, 3e4, 1.0, 1e-7, 1e-30], np.float32)
     qf = qf * factors[None, :, None]
