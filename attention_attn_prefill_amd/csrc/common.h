@@ -50,6 +50,15 @@ __device__ __forceinline__ void lds_dma_16(const void* g, uint32_t lds_off) {
                : "memory", "m0");
 }
 
+// As lds_dma_16 with the address split into a wave-uniform 64-bit base (SGPRs) and a 32-bit
+// per-lane byte offset: a tile loop then advances the base with scalar arithmetic and keeps
+// the offsets fixed, instead of recomputing 64-bit lane addresses with vector instructions.
+__device__ __forceinline__ void lds_dma_16s(const void* sbase, uint32_t voff, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_off), "v"(voff),
+               "s"(sbase)
+               : "memory", "m0");
+}
+
 // As lds_dma_16 with one dword per lane: LDS byte address lds_off + 4 * lane.
 __device__ __forceinline__ void lds_dma_4(const void* g, uint32_t lds_off) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_off), "v"(g)

@@ -160,12 +160,9 @@ __global__ __launch_bounds__(kPrefillThreads, D == 128 ? 3 : 2) void prefill_bf1
   // k0 * row stride. Paged: one 1 KB load instruction stays inside one 16-key block (16 is a
   // multiple of the rows per instruction), so its block comes from one wave-uniform table
   // lookup; the lane adds its slot and chunk.
-  int64_t koff[T::PER_WAVE], voff[T::PER_WAVE];
-#pragma unroll
-  for (int i = 0; i < T::PER_WAVE; ++i) {
-    koff[i] = (int64_t)(ld_row0 + i * ROW_STEP) * kv_row_stride + 8 * ld_kchunk;
-    voff[i] = (int64_t)(ld_row0 + i * ROW_STEP) * kv_row_stride + 8 * ld_vchunk;
-  }
+  // byte offsets of this lane's 16 bytes from the base of its instruction's first row
+  const uint32_t ld_koff = (uint32_t)(((int64_t)ld_row0 * kv_row_stride + 8 * ld_kchunk) * 2);
+  const uint32_t ld_voff = (uint32_t)(((int64_t)ld_row0 * kv_row_stride + 8 * ld_vchunk) * 2);
   const int pg_slot_k = (ld_row0 & 15) * D + 8 * ld_kchunk;
   const int pg_slot_v = (ld_row0 & 15) * D + 8 * ld_vchunk;
   const int pg_blk0 = __builtin_amdgcn_readfirstlane(ld_row0 >> 4);
@@ -198,12 +195,12 @@ __global__ __launch_bounds__(kPrefillThreads, D == 128 ? 3 : 2) void prefill_bf1
         lds_dma_16(vs, lds_addr(vdst + i * 4096));
       }
     } else if (k0 + kBN <= S) {
-      const uint16_t* kt = kbase + (int64_t)k0 * kv_row_stride;
-      const uint16_t* vt = vbase + (int64_t)k0 * kv_row_stride;
+      // uniform row base in SGPRs, fixed per-lane byte offsets (rows ld_row0 + i*ROW_STEP)
 #pragma unroll
       for (int i = 0; i < T::PER_WAVE; ++i) {
-        lds_dma_16(kt + koff[i], lds_addr(kdst + i * 4096));
-        lds_dma_16(vt + voff[i], lds_addr(vdst + i * 4096));
+        const int64_t rbase = (int64_t)(k0 + i * ROW_STEP) * kv_row_stride;
+        lds_dma_16s(kbase + rbase, ld_koff, lds_addr(kdst + i * 4096));
+        lds_dma_16s(vbase + rbase, ld_voff, lds_addr(vdst + i * 4096));
       }
     } else {
 #pragma unroll
@@ -245,7 +242,7 @@ __global__ __launch_bounds__(kPrefillThreads, D == 128 ? 3 : 2) void prefill_bf1
   // in the loop: separate masked/unmasked copies, or skipping the step on some paths, make
   // the compiler merge the O accumulators from several paths into registers that are not the
   // MFMA's tuples, and it then copies all of them every tile.
-  auto tile_step = [&](const char* st_base, int k0, bool masked) {
+  auto tile_step = [&](const char* st_base, int k0, bool masked, bool dummy) {
     // S^T = K Q^T; the two 32-key blocks alternate so consecutive MFMAs are independent
     // (a dependent accumulation chain would wait for each result)
     f32x16 sacc[kBN / 32];
@@ -265,6 +262,7 @@ __global__ __launch_bounds__(kPrefillThreads, D == 128 ? 3 : 2) void prefill_bf1
       const int qp = off + q0w + col;  // query position
       int hi = Lk - 1 - k0;
       if (causal) hi = min(hi, qp - k0);
+      if (dummy) hi = -(1 << 30);  // the leading stand-in tile: every score masked
       const int lo_off = window > 0 ? qp - window + 1 - k0 : -(1 << 30);
       const int hi4 = hi - 4 * half, lo4 = lo_off - 4 * half;
 #pragma unroll
@@ -318,7 +316,12 @@ __global__ __launch_bounds__(kPrefillThreads, D == 128 ? 3 : 2) void prefill_bf1
       }
   };
 
-  if (jlo <= jhi) issue_tile(jlo, 0);
+  // The tile loop below is unrolled over the two LDS stages, so that each stage's operand
+  // addresses are immediates; an odd number of tiles gets one stand-in tile in front (tile
+  // jlo - 1, whose keys no row of the workgroup sees, or tile 0 again when jlo = 0), fully
+  // masked: it adds nothing and triggers no rescale.
+  const int jstart = jlo - ((jhi - jlo + 1) & 1);
+  if (jlo <= jhi) issue_tile(max(jstart, 0), 0);
 
   if constexpr (PAGED) {
     // The chunk's rows of this workgroup (one head sub-group per KV head writes) go to their
@@ -346,8 +349,8 @@ __global__ __launch_bounds__(kPrefillThreads, D == 128 ? 3 : 2) void prefill_bf1
     }
   }
 
-  for (int j = jlo; j <= jhi; ++j) {
-    const int st = (j - jlo) & 1;
+  auto body = [&](int j, auto stage) {
+    constexpr int st = decltype(stage)::value;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile-j loads have landed
     __syncthreads();                     // ... and everyone's; stage st^1 is no longer read
     if (j < jhi) issue_tile(j + 1, st ^ 1);
@@ -369,10 +372,15 @@ __global__ __launch_bounds__(kPrefillThreads, D == 128 ? 3 : 2) void prefill_bf1
     }
     // A tile outside this wave's key range (other waves of the workgroup need it) runs
     // masked: every score is -inf, so it adds nothing and triggers no rescale.
+    const bool dummy = j < jlo;
     const bool relevant = wave_live && k0 <= kmax_w && k0 + kBN - 1 >= kmin_w;
-    const bool full = relevant && (!causal || k0 + kBN - 1 <= off + q0w) &&
+    const bool full = !dummy && relevant && (!causal || k0 + kBN - 1 <= off + q0w) &&
                       (window == 0 || off + qw_last - k0 < window) && (k0 + kBN <= Lk);
-    tile_step(smem + st * T::STAGE, k0, !full);
+    tile_step(smem + st * T::STAGE, k0, !full, dummy);
+  };
+  for (int j = jstart; j <= jhi; j += 2) {
+    body(j, std::integral_constant<int, 0>{});
+    body(j + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: O = O^T / l, bf16 RNE ---------------------------------------------------
