@@ -156,11 +156,11 @@ __global__ __launch_bounds__(kPrefillThreads, D == 128 ? 3 : 2) void prefill_bf1
   const int64_t kv_row_stride = (int64_t)Hkv * D;
   const uint16_t* kbase = k + ((int64_t)b * S * Hkv + g) * D;
   const uint16_t* vbase = v + ((int64_t)b * S * Hkv + g) * D;
-  // Contiguous: per-lane element offsets of this wave's rows at k0 = 0; a tile adds
-  // k0 * row stride. Paged: one 1 KB load instruction stays inside one 16-key block (16 is a
-  // multiple of the rows per instruction), so its block comes from one wave-uniform table
-  // lookup; the lane adds its slot and chunk.
-  // byte offsets of this lane's 16 bytes from the base of its instruction's first row
+  // Contiguous: a load instruction's first row gives a wave-uniform base (SGPRs, advanced by
+  // scalar arithmetic per tile) and the lane adds a fixed byte offset (its row within the
+  // instruction and its chunk). Paged: one 1 KB load instruction stays inside one 16-key block
+  // (16 is a multiple of the rows per instruction), so its block comes from one wave-uniform
+  // table lookup; the lane adds its slot and chunk.
   const uint32_t ld_koff = (uint32_t)(((int64_t)ld_row0 * kv_row_stride + 8 * ld_kchunk) * 2);
   const uint32_t ld_voff = (uint32_t)(((int64_t)ld_row0 * kv_row_stride + 8 * ld_vchunk) * 2);
   const int pg_slot_k = (ld_row0 & 15) * D + 8 * ld_kchunk;
@@ -179,20 +179,23 @@ __global__ __launch_bounds__(kPrefillThreads, D == 128 ? 3 : 2) void prefill_bf1
         int pb = lb < pg_nblk ? trow[lb] : 0;  // blocks past the context: any valid block
         if (pb < 0 || pb >= pg.num_blocks) pb = 0;  // unusable entry: never dereferenced
         const int64_t boff = ((int64_t)pb * Hkv + g) * 16 * D;
-        const uint16_t* ks = k + boff + pg_slot_k;
-        const uint16_t* vs = v + boff + pg_slot_v;
         if (pg.k_new != nullptr && k0 + kBN > off) {
           // the chunk's own keys (positions off ..) come from its rows; keys past the
           // context read the last row (their scores are masked, their V rows zeroed)
+          const uint16_t* ks = k + boff + pg_slot_k;
+          const uint16_t* vs = v + boff + pg_slot_v;
           const int key = k0 + ld_row0 + i * ROW_STEP;
           if (key >= off) {
             const int64_t nrow = ((int64_t)(q_row0 + min(key, Lk - 1) - off) * Hkv + g) * D;
             ks = pg.k_new + nrow + 8 * ld_kchunk;
             vs = pg.v_new + nrow + 8 * ld_vchunk;
           }
+          lds_dma_16(ks, lds_addr(kdst + i * 4096));
+          lds_dma_16(vs, lds_addr(vdst + i * 4096));
+        } else {  // the block's base is wave-uniform: SGPR base, fixed lane offsets
+          lds_dma_16s(k + boff, 2u * pg_slot_k, lds_addr(kdst + i * 4096));
+          lds_dma_16s(v + boff, 2u * pg_slot_v, lds_addr(vdst + i * 4096));
         }
-        lds_dma_16(ks, lds_addr(kdst + i * 4096));
-        lds_dma_16(vs, lds_addr(vdst + i * 4096));
       }
     } else if (k0 + kBN <= S) {
       // uniform row base in SGPRs, fixed per-lane byte offsets (rows ld_row0 + i*ROW_STEP)
