@@ -120,8 +120,6 @@ __global__ __launch_bounds__(kPrefillThreads, D == 128 ? 3 : 2) void prefill_bf1
   const int jlo = kmin / kBN, jhi = kmax / kBN;
   const bool wave_live = q0w < Sq;
   const int qw_last = min(Sq - 1, q0w + 31);
-  const int kmin_w = window > 0 ? max(0, off + q0w - window + 1) : 0;
-  const int kmax_w = causal ? off + qw_last : Lk - 1;
 
   // ---- Q^T fragments (B operand), kept in registers --------------------------------------
   constexpr int QSTEPS = D / 16;
@@ -167,7 +165,11 @@ __global__ __launch_bounds__(kPrefillThreads, D == 128 ? 3 : 2) void prefill_bf1
   const int pg_slot_v = (ld_row0 & 15) * D + 8 * ld_vchunk;
   const int pg_blk0 = __builtin_amdgcn_readfirstlane(ld_row0 >> 4);
   const int pg_nblk = (Lk + 15) >> 4;
-  auto issue_tile = [&](int j, int stage) {
+  // contiguous rows: element offset between consecutive tiles and between this wave's rows
+  const int64_t tile_stride = (int64_t)kBN * kv_row_stride;
+  const int64_t row_step_off = (int64_t)ROW_STEP * kv_row_stride;
+  // tile j starts at element offset toff = j * tile_stride of the sequence's K/V (contiguous)
+  auto issue_tile = [&](int j, int stage, int64_t toff) {
     const int k0 = j * kBN;
     char* kdst = smem + stage * T::STAGE + wave * 1024;
     char* vdst = kdst + T::TILE;
@@ -201,7 +203,7 @@ __global__ __launch_bounds__(kPrefillThreads, D == 128 ? 3 : 2) void prefill_bf1
       // uniform row base in SGPRs, fixed per-lane byte offsets (rows ld_row0 + i*ROW_STEP)
 #pragma unroll
       for (int i = 0; i < T::PER_WAVE; ++i) {
-        const int64_t rbase = (int64_t)(k0 + i * ROW_STEP) * kv_row_stride;
+        const int64_t rbase = toff + i * row_step_off;
         lds_dma_16s(kbase + rbase, ld_koff, lds_addr(kdst + i * 4096));
         lds_dma_16s(vbase + rbase, ld_voff, lds_addr(vdst + i * 4096));
       }
@@ -324,7 +326,20 @@ __global__ __launch_bounds__(kPrefillThreads, D == 128 ? 3 : 2) void prefill_bf1
   // jlo - 1, whose keys no row of the workgroup sees, or tile 0 again when jlo = 0), fully
   // masked: it adds nothing and triggers no rescale.
   const int jstart = jlo - ((jhi - jlo + 1) & 1);
-  if (jlo <= jhi) issue_tile(max(jstart, 0), 0);
+  if (jlo <= jhi) issue_tile(max(jstart, 0), 0, (int64_t)max(jstart, 0) * tile_stride);
+  int64_t next_toff = (int64_t)(jstart + 1) * tile_stride;  // offset of the tile issued next
+
+  // Tiles jf_lo .. jf_hi are visible whole to every row of this wave (causal limit, window,
+  // end of the keys), so they run without per-score masks. Every other tile the workgroup
+  // visits is masked: an edge tile, or one outside this wave's key range that another wave
+  // needs (every score -inf: it adds nothing and triggers no rescale).
+  auto floor_div = [](int a, int n) { return a >= 0 ? a / n : -((n - 1 - a) / n); };
+  int jf_lo = 0, jf_hi = -1;
+  if (wave_live) {
+    jf_hi = floor_div(Lk - kBN, kBN);
+    if (causal) jf_hi = min(jf_hi, floor_div(off + q0w - kBN + 1, kBN));
+    if (window > 0) jf_lo = max(jf_lo, -floor_div(window - 1 - off - qw_last, kBN));
+  }
 
   if constexpr (PAGED) {
     // The chunk's rows of this workgroup (one head sub-group per KV head writes) go to their
@@ -356,7 +371,8 @@ __global__ __launch_bounds__(kPrefillThreads, D == 128 ? 3 : 2) void prefill_bf1
     constexpr int st = decltype(stage)::value;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile-j loads have landed
     __syncthreads();                     // ... and everyone's; stage st^1 is no longer read
-    if (j < jhi) issue_tile(j + 1, st ^ 1);
+    if (j < jhi) issue_tile(j + 1, st ^ 1, next_toff);
+    next_toff += tile_stride;
 
     const int k0 = j * kBN;
     if constexpr (PAGED) {
@@ -373,12 +389,8 @@ __global__ __launch_bounds__(kPrefillThreads, D == 128 ? 3 : 2) void prefill_bf1
         __syncthreads();
       }
     }
-    // A tile outside this wave's key range (other waves of the workgroup need it) runs
-    // masked: every score is -inf, so it adds nothing and triggers no rescale.
     const bool dummy = j < jlo;
-    const bool relevant = wave_live && k0 <= kmax_w && k0 + kBN - 1 >= kmin_w;
-    const bool full = !dummy && relevant && (!causal || k0 + kBN - 1 <= off + q0w) &&
-                      (window == 0 || off + qw_last - k0 < window) && (k0 + kBN <= Lk);
+    const bool full = !dummy && j >= jf_lo && j <= jf_hi;
     tile_step(smem + st * T::STAGE, k0, !full, dummy);
   };
   for (int j = jstart; j <= jhi; j += 2) {
