@@ -141,6 +141,7 @@ __global__ __launch_bounds__(kPrefillThreads, D == 128 ? 3 : 2) void prefill_bf1
   for (int i = 0; i < DB; ++i)
     oacc[i] = (f32x16){};
   float m_run = kNegBig, l_run = 0.f;
+  float m_thr = kNegBig + kRescaleSlack;  // rescale when a tile's max exceeds this
 
   // ---- direct global -> LDS tile loads ---------------------------------------------------
   // Wave instruction n (of INSTR per tile) writes LDS bytes [1024n, 1024n + 1024) of the tile;
@@ -284,11 +285,12 @@ __global__ __launch_bounds__(kPrefillThreads, D == 128 ? 3 : 2) void prefill_bf1
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
     mx = xhalf_max(mx) * scale_log2;
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
+    if (__builtin_amdgcn_ballot_w64(mx > m_thr) != 0) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = fast_exp2(m_run - m_new);
       l_run *= alpha;
       m_run = m_new;
+      m_thr = m_new + kRescaleSlack;
 #pragma unroll
       for (int i = 0; i < DB; ++i)
         oacc[i] *= alpha;

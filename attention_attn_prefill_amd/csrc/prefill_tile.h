@@ -15,10 +15,14 @@ constexpr float kRescaleSlack = 8.0f;
 
 __device__ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-// max / sum over lanes l and l ^ 32 (the two halves of a 32x32 accumulator column)
+// max / sum over lanes l and l ^ 32 (the two halves of a 32x32 accumulator column). The max is
+// one v_max_f32 written out: fmaxf would first quiet both inputs (the exchanged value is not
+// known to be canonical), two more instructions; scores are never NaN.
 __device__ __forceinline__ float xhalf_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  float m;
+  asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(__uint_as_float(r[0])), "v"(__uint_as_float(r[1])));
+  return m;
 }
 __device__ __forceinline__ float xhalf_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
