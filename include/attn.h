@@ -52,7 +52,7 @@ enum attn_status {
   ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
   ATTN_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
   ATTN_ERR_DTYPE = 3,       /* unknown dtype code */
-  ATTN_ERR_UNSUPPORTED = 4, /* valid request that this build does not implement */
+  ATTN_ERR_UNSUPPORTED = 4, /* valid request that the library does not implement */
   ATTN_ERR_WORKSPACE = 5,   /* workspace missing or smaller than attn_decode_workspace_size() */
   ATTN_ERR_HIP = 6          /* a HIP launch failed; attn_last_error() holds the HIP message */
 };
