@@ -29,7 +29,9 @@
  *
  * Conventions for every call:
  *  - Every tensor argument is a device pointer owned by the caller; the library allocates no
- *    memory and keeps no state beyond a thread-local last-error string.
+ *    memory. Its only state is a thread-local last-error string, kernel attributes set once
+ *    per device, and the static scratch array of attn_decode_paged_noalloc (part of the code
+ *    object) with its per-device address.
  *  - Every call only enqueues work on `stream` (a hipStream_t; NULL = the default stream) and
  *    returns without synchronising. The result is ready when the stream reaches that point.
  *  - Arguments are validated on the host before any launch; on a nonzero return nothing was
