@@ -110,16 +110,20 @@ int attn_prefill_paged(const void* q, const void* k_new, const void* v_new, void
     return fail(ATTN_ERR_NULL, "q, k_cache, v_cache, block_table, cu_q, context_lens and o are required");
   attn::PrefillPagedArgs a{q, k_new, v_new, k_cache, v_cache, block_table, cu_q, context_lens,
                            o, lse, B, Hq, Hkv, D, max_blocks_per_seq, num_blocks, max_q_len,
-                           total_q, scale, causal != 0, window};
+                           total_q, scale, causal != 0, window, 0};
   attn::launch_prefill_paged(a, reinterpret_cast<hipStream_t>(stream));
   return check_launch("attn_prefill_paged");
 }
+
+// query columns ((Hq / Hkv) * q_len) one decode wave holds: one MFMA tile
+constexpr int kMaxDecodeCols = 16;
 
 static size_t decode_workspace(int B, int q_len, int Hq, int Hkv, int D, int max_context_len,
                                int window, int split_tokens) {
   if (B < 1 || q_len < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || max_context_len < 1 || window < 0 ||
       split_tokens < 0)
     return 0;
+  if (Hq / Hkv * q_len > kMaxDecodeCols) return 0;  // prefill-kernel path: no workspace
   return attn::plan_decode(B, q_len, Hq, Hkv, D, max_context_len, window, split_tokens)
       .workspace_bytes;
 }
@@ -161,11 +165,29 @@ static int decode_impl(const char* who, const void* q, const void* k_cache, cons
   if (!(std::isfinite(scale) && scale > 0.f)) return fail(ATTN_ERR_SHAPE, "scale must be finite and > 0");
   if (!supported_d(D)) return fail(ATTN_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
   if (block_size != 16) return fail(ATTN_ERR_UNSUPPORTED, "block_size %d (supported: 16)", block_size);
-  if (Hq / Hkv * q_len > 16)
-    return fail(ATTN_ERR_UNSUPPORTED, "(Hq/Hkv) * q_len = %d > 16", Hq / Hkv * q_len);
   if (split_tokens % block_size != 0) return fail(ATTN_ERR_SHAPE, "split_tokens %d is not a multiple of block_size", split_tokens);
   if (split_tokens > attn::kMaxSplitTokens)
     return fail(ATTN_ERR_UNSUPPORTED, "split_tokens %d > %d", split_tokens, attn::kMaxSplitTokens);
+  if (Hq / Hkv * q_len > kMaxDecodeCols) {
+    // More query columns per KV head than one decode MFMA tile holds: the rows are a fixed-size
+    // chunk per sequence, computed by the paged prefill kernel (bf16 caches; it reads the cache
+    // through the same block table, K/V once per workgroup of query heads).
+    if (kv_dtype != ATTN_BF16)
+      return fail(ATTN_ERR_UNSUPPORTED, "(Hq/Hkv) * q_len = %d > %d needs a bf16 cache",
+                  Hq / Hkv * q_len, kMaxDecodeCols);
+    if (B > 65535) return fail(ATTN_ERR_SHAPE, "B must be <= 65535");
+    if ((long long)max_blocks_per_seq * block_size > 0x7fffffffLL)
+      return fail(ATTN_ERR_SHAPE, "max_blocks_per_seq * block_size overflows int32");
+    if (attn::prefill_workgroups(B, q_len, Hq, Hkv) * attn::prefill_threads_per_workgroup() >=
+        (1LL << 32))
+      return fail(ATTN_ERR_SHAPE, "B * Hq * q_len too large for one launch");
+    attn::PrefillPagedArgs a{q, nullptr, nullptr, const_cast<void*>(k_cache),
+                             const_cast<void*>(v_cache), block_table, nullptr, context_lens, o,
+                             nullptr, B, Hq, Hkv, D, max_blocks_per_seq, num_blocks, q_len,
+                             B * q_len, scale, 1, window, q_len};
+    attn::launch_prefill_paged(a, reinterpret_cast<hipStream_t>(stream));
+    return check_launch(who);
+  }
   if (B > 65535 / q_len || Hkv > 65535) return fail(ATTN_ERR_SHAPE, "B * q_len and Hkv must be <= 65535");
   attn::DecodePlan plan =
       attn::plan_decode(B, q_len, Hq, Hkv, D, max_context_len, window, split_tokens);

@@ -76,13 +76,17 @@ struct PrefillPagedArgs {
   void* k_cache;
   void* v_cache;
   const int32_t* table;
-  const int32_t* cu_q;  // [B + 1]
+  const int32_t* cu_q;  // [B + 1], or null with fixed_q > 0
   const int32_t* ctx;   // [B]
   void* o;
   float* lse;  // [total_q][Hq] or null
   int B, Hq, Hkv, D, max_blocks_per_seq, num_blocks, max_q_len, total_q;
   float scale;
   int causal, window;
+  // > 0: every sequence has exactly fixed_q rows (rows b*fixed_q ..), row i at position
+  // ctx - fixed_q + i even when that is negative (such rows see no key and get zeros): the
+  // layout and row semantics of multi-row decode
+  int fixed_q;
 };
 
 DecodePlan plan_decode(int B, int q_len, int Hq, int Hkv, int D, int max_context_len, int window,

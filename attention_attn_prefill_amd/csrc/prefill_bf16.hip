@@ -54,6 +54,9 @@ struct PagedArgs {
   const uint16_t* v_new;
   uint16_t* k_cache;  // the caches again, for the chunk's slots (written, never read here)
   uint16_t* v_cache;
+  // > 0: fixed_q rows per sequence, no cu_q; a row whose position ctx - fixed_q + i is
+  // negative sees no key and is written as zeros (multi-row decode semantics)
+  int fixed_q;
 };
 
 template <int D, bool PAGED>
@@ -102,11 +105,16 @@ __global__ __launch_bounds__(kPrefillThreads, D == 128 ? 3 : 2) void prefill_bf1
   // Sq query rows at positions off + r against Lk keys (contiguous: Sq = Lk = S, off = 0)
   int Sq = S, Lk = S, q_row0 = b * S;
   if constexpr (PAGED) {
-    q_row0 = pg.cu_q[b];
     Lk = min(max(pg.ctx[b], 0), pg.max_blocks * 16);
-    Sq = min(pg.cu_q[b + 1] - q_row0, Lk);  // rows past the context are not computed
+    if (pg.fixed_q > 0) {
+      q_row0 = b * pg.fixed_q;
+      Sq = pg.fixed_q;
+    } else {
+      q_row0 = pg.cu_q[b];
+      Sq = min(pg.cu_q[b + 1] - q_row0, Lk);  // rows past the context are not computed
+    }
   }
-  const int off = Lk - Sq;
+  const int off = Lk - Sq;  // negative only with fixed_q rows that precede the sequence
   const int rows = 32 * QW;
   const int q0 = qblk * rows;
   if (q0 >= Sq) return;  // whole workgroup: nothing to do for this sequence
@@ -403,7 +411,7 @@ __global__ __launch_bounds__(kPrefillThreads, D == 128 ? 3 : 2) void prefill_bf1
   // ---- epilogue: O = O^T / l, bf16 RNE ---------------------------------------------------
   const int qr = q0w + col;
   if (wave_live && qr < Sq) {
-    const float inv = 1.0f / l_run;
+    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;  // a row with no visible key: zeros
     uint16_t* orow = o + (((int64_t)q_row0 + qr) * Hq + head) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -463,7 +471,7 @@ static void launch_d(const void* q, const void* k, const void* v, void* o, float
 }
 
 int launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
-  const PagedArgs none{nullptr, nullptr, nullptr, 0, 0, nullptr, nullptr, nullptr, nullptr};
+  const PagedArgs none{nullptr, nullptr, nullptr, 0, 0, nullptr, nullptr, nullptr, nullptr, 0};
   if (a.D == 64)
     launch_d<64, false>(a.q, a.k, a.v, a.o, a.lse, a.B, a.S, a.Hq, a.Hkv, a.scale, a.causal,
                         a.window, none, stream);
@@ -483,7 +491,8 @@ int launch_prefill_paged(const PrefillPagedArgs& a, hipStream_t stream) {
                      (const uint16_t*)a.k_new,
                      (const uint16_t*)a.v_new,
                      (uint16_t*)a.k_cache,
-                     (uint16_t*)a.v_cache};
+                     (uint16_t*)a.v_cache,
+                     a.fixed_q};
   if (a.D == 64)
     launch_d<64, true>(a.q, a.k_cache, a.v_cache, a.o, a.lse, a.B, a.max_q_len, a.Hq, a.Hkv,
                        a.scale, a.causal, a.window, pg, stream);

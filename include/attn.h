@@ -169,9 +169,11 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_context
  *  workspace    : device buffer of at least attn_decode_workspace_size(...) bytes (may be NULL
  *                 when that size is 0); overwritten by the call; its contents on entry do not
  *                 matter. Two calls in flight at once must not share a workspace.
- *  Requirements: D in {64, 128}; block_size == 16; Hq % Hkv == 0 and Hq / Hkv <= 16;
- *                 q, o, k_cache, v_cache, k_scale and v_scale 16-byte aligned (else
- *                 ATTN_ERR_SHAPE).
+ *  Requirements: D in {64, 128}; block_size == 16; Hq % Hkv == 0; Hq / Hkv <= 16 with an
+ *                 INT8 or FP8 cache (ATTN_ERR_UNSUPPORTED above; a bf16 cache with more query
+ *                 heads per KV head is computed by the paged prefill kernel, as in
+ *                 attn_decode_paged_multi); q, o, k_cache, v_cache, k_scale and v_scale
+ *                 16-byte aligned (else ATTN_ERR_SHAPE).
  */
 int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       const void* k_scale, const void* v_scale,
@@ -225,9 +227,13 @@ size_t attn_decode_multi_workspace_size(int B, int q_len, int Hq, int Hkv, int D
  *                 (and, with a window, only the last `window` of them). The q_len draft tokens'
  *                 K/V must already be in the cache (kv_cache_append), so context_lens counts
  *                 them; rows whose position is negative produce zeros.
- *  q_len        : >= 1, with (Hq / Hkv) * q_len <= 16 (ATTN_ERR_UNSUPPORTED above): the query
- *                 heads of one KV head times the rows share one MFMA tile, so each K/V byte is
- *                 still read once. Longer drafts: use attn_prefill_paged.
+ *  q_len        : >= 1. Up to (Hq / Hkv) * q_len = 16 query columns per KV head the rows and
+ *                 heads share one MFMA tile of the decode kernels, so each K/V byte is read
+ *                 once for all of them. Above 16 (e.g. 8 draft tokens at 4 query heads per KV
+ *                 head) a bf16 cache is read by the paged prefill kernel instead (the rows of a
+ *                 sequence as one fixed-size chunk, same row positions and zeros; no workspace,
+ *                 split_tokens has no effect, context_lens is clamped to the table's capacity
+ *                 only); an INT8 or FP8 cache returns ATTN_ERR_UNSUPPORTED there.
  *  workspace    : at least attn_decode_multi_workspace_size(...) bytes.
  * q_len == 1 computes exactly what attn_decode_paged computes.
  */

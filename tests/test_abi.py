@@ -83,7 +83,9 @@ def _decode(**kw):
     (dict(ks=FAKE, vs=FAKE), A.ATTN_ERR_SHAPE), (dict(Hq=6, Hkv=4), A.ATTN_ERR_SHAPE),
     (dict(maxctx=0), A.ATTN_ERR_SHAPE), (dict(window=-2), A.ATTN_ERR_SHAPE), (dict(split=-16), A.ATTN_ERR_SHAPE),
     (dict(split=24), A.ATTN_ERR_SHAPE), (dict(D=80), A.ATTN_ERR_UNSUPPORTED), (dict(bs=8), A.ATTN_ERR_UNSUPPORTED),
-    (dict(Hq=34, Hkv=2), A.ATTN_ERR_UNSUPPORTED), (dict(split=8208), A.ATTN_ERR_UNSUPPORTED),
+    # more than 16 query heads per KV head: only bf16 caches (through the prefill kernel)
+    (dict(Hq=34, Hkv=2, kv=A.ATTN_I8, ks=FAKE, vs=FAKE), A.ATTN_ERR_UNSUPPORTED),
+    (dict(split=8208), A.ATTN_ERR_UNSUPPORTED),
     (dict(maxctx=5000, split=64), A.ATTN_ERR_WORKSPACE),
     (dict(maxctx=5000, split=64, ws=FAKE, wsb=16), A.ATTN_ERR_WORKSPACE),
     # every tensor the kernels read or write in 16-byte pieces must be 16-byte aligned
@@ -108,13 +110,26 @@ def _multi(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), A.ATTN_ERR_NULL), (dict(ql=0), A.ATTN_ERR_SHAPE), (dict(ql=-1), A.ATTN_ERR_SHAPE),
-    (dict(ql=5), A.ATTN_ERR_UNSUPPORTED),               # 4 heads per KV head x 5 rows > 16
-    (dict(Hq=16, Hkv=1, ql=2), A.ATTN_ERR_UNSUPPORTED), (dict(B=40000), A.ATTN_ERR_SHAPE),
+    # 4 heads per KV head x 5 rows > 16 columns: a byte cache is refused (a bf16 cache goes
+    # through the prefill kernel)
+    (dict(ql=5, kv=A.ATTN_I8, ks=FAKE, vs=FAKE), A.ATTN_ERR_UNSUPPORTED),
+    (dict(Hq=16, Hkv=1, ql=2, kv=A.ATTN_FP8, ks=FAKE, vs=FAKE), A.ATTN_ERR_UNSUPPORTED),
+    (dict(ql=5, split=24), A.ATTN_ERR_SHAPE), (dict(ql=5, window=-1), A.ATTN_ERR_SHAPE),
+    (dict(B=40000), A.ATTN_ERR_SHAPE), (dict(ql=5, B=70000), A.ATTN_ERR_SHAPE),
     (dict(), A.ATTN_ERR_WORKSPACE),                     # the balanced shape stages partials
     (dict(kv=A.ATTN_FP8, ks=ctypes.c_void_p(0x1008), vs=FAKE), A.ATTN_ERR_SHAPE),
 ])
 def test_decode_multi_validation(kw, code):
     assert _multi(**kw) == code
+
+
+def test_wide_multi_row_decode_needs_no_workspace():
+    """More than 16 query columns per KV head run on the prefill kernel: no workspace."""
+    wm = A.attn_decode_multi_workspace_size
+    assert wm(3, 8, 32, 8, 64, 4096, 0, 0) == 0    # 4 heads x 8 rows
+    assert wm(3, 5, 20, 4, 128, 700, 100, 0) == 0  # 5 heads x 5 rows
+    assert A.attn_decode_workspace_size(3, 64, 2, 64, 4096, 0, 0) == 0  # 32 heads per KV head
+    assert wm(3, 4, 32, 8, 64, 4096, 0, 0) > 0     # 16 columns: the decode kernels
 
 
 def test_multi_workspace_matches_single_row():
