@@ -42,7 +42,9 @@ def _poison_unused(pool_arr, table, ctx, bs=16, value=None):
 
 
 CASES = [(64, 8, 2, 0), (64, 32, 8, 5), (128, 8, 1, 0), (128, 4, 4, 40), (64, 16, 1, 0),
-         (128, 64, 8, 0), (64, 6, 3, 17)]
+         (128, 64, 8, 0), (64, 6, 3, 17),
+         # more than 16 query heads per KV head: the paged prefill kernel's path
+         (64, 64, 2, 0), (128, 40, 2, 17)]
 
 
 @pytest.mark.parametrize("split", [0, 16, 48])
