@@ -181,6 +181,8 @@ static int decode_impl(const char* who, const void* q, const void* k_cache, cons
     if (attn::prefill_workgroups(B, q_len, Hq, Hkv) * attn::prefill_threads_per_workgroup() >=
         (1LL << 32))
       return fail(ATTN_ERR_SHAPE, "B * Hq * q_len too large for one launch");
+    // no k_new / v_new: the kernel only reads the caches (their pointers are non-const in the
+    // argument block for the append the paged prefill can fuse)
     attn::PrefillPagedArgs a{q, nullptr, nullptr, const_cast<void*>(k_cache),
                              const_cast<void*>(v_cache), block_table, nullptr, context_lens, o,
                              nullptr, B, Hq, Hkv, D, max_blocks_per_seq, num_blocks, q_len,
