@@ -41,8 +41,24 @@ def _decode_case(i):
                 seed=9000 + i)
 
 
+def _wide_decode_case(i):
+    """Draft rows x query heads per KV head above 16 (bf16 cache): the paged prefill kernel's
+    path of attn_decode_paged / attn_decode_paged_multi."""
+    r = np.random.default_rng(9300 + i)
+    QL = int(r.choice([1, 2, 3, 5, 6, 8]))
+    G = int(r.choice([g for g in (3, 4, 5, 6, 8, 12, 16, 20, 32) if 16 < g * QL <= 64]))
+    B = int(r.integers(1, 9))
+    ctx = [int(r.integers(QL, 41)) if r.random() < 0.3 else int(r.integers(max(QL, 41), 1201))
+           for _ in range(B)]
+    window = 0 if r.random() < 0.6 else int(r.integers(1, 401))
+    return dict(D=int(r.choice([64, 128])), Hkv=int(r.choice([1, 2, 4])), G=G, QL=QL, ctx=tuple(ctx),
+                window=window, kv="bf16", split=0 if r.random() < 0.5 else 16 * int(r.integers(1, 9)),
+                spare=int(r.integers(0, 4)), seed=9300 + i)
+
+
 SCALE = max(1, int(os.environ.get("ATTN_RANDOM_SCALE", "1")))
-DECODE_CASES = [_decode_case(i) for i in range(60 * SCALE)]
+DECODE_CASES = [_decode_case(i) for i in range(60 * SCALE)] + \
+    [_wide_decode_case(i) for i in range(15 * SCALE)]
 
 
 def _dec_id(c):
