@@ -166,3 +166,27 @@ def test_int8_append_and_decode_blocks_above_4gib():
     assert maxabs(host_f64(o), ro) <= BF16_TOL
     del kc, vc, ks, vs
     t.cuda.empty_cache()
+
+
+def test_prefill_contiguous_tensors_above_4gib():
+    """Contiguous prefill with Q, K, V and O of 4.4 GB each (130 x 16384 rows, 8 heads, D = 128,
+    causal window 32): rows of the batches whose offsets pass 2^31 and 2^32 bytes."""
+    import attention_attn_prefill_amd as A
+    t = torch()
+    B, S, H, W = 130, 16384, 8, 32
+    gen = t.Generator(device="cuda").manual_seed(4700)
+    q, k, v = (t.randn((B, S, H, D), device="cuda", generator=gen, dtype=t.bfloat16) for _ in range(3))
+    assert q.numel() * 2 > (1 << 32)
+    L = t.empty((B, H, S), dtype=t.float32, device="cuda")
+    o = A.attn_prefill(q, k, v, causal=True, window=W, lse=L)
+    t.cuda.synchronize()
+    rows = [0, 1, 31, 32, 33, 1000, 8191, 16383]
+    for b in (64, 129):  # row offsets past 2^31 and past 2^32 bytes
+        for h in (0, 7):
+            qs = host_f64(q[b, rows, h])
+            ks, vs = host_f64(k[b, :, h]), host_f64(v[b, :, h])
+            ro, rl = oracle.attention_head(qs, ks, vs, D ** -0.5, rows, True, W)
+            assert maxabs(host_f64(o[b, rows, h]), ro) <= BF16_TOL, (b, h)
+            assert maxabs(host_f64(L[b, h, rows]), rl) <= LSE_TOL_BF16, (b, h)
+    del q, k, v, o, L
+    t.cuda.empty_cache()
