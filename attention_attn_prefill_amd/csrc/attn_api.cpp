@@ -118,13 +118,26 @@ int attn_prefill_paged(const void* q, const void* k_new, const void* v_new, void
 // query columns ((Hq / Hkv) * q_len) one decode wave holds: one MFMA tile
 constexpr int kMaxDecodeCols = 16;
 
+// More columns than that with an INT8 / FP8 cache: each cache head serves R virtual KV heads of
+// (Hq / Hkv) / R query heads, R the smallest divisor of Hq / Hkv that brings a virtual head's
+// columns to kMaxDecodeCols or fewer (the cache head is then read R times). 0: none exists
+// (q_len > kMaxDecodeCols).
+static int byte_cache_kv_rep(int G, int q_len) {
+  for (int R = 1; R <= G; ++R)
+    if (G % R == 0 && (G / R) * q_len <= kMaxDecodeCols) return R;
+  return 0;
+}
+
 static size_t decode_workspace(int B, int q_len, int Hq, int Hkv, int D, int max_context_len,
                                int window, int split_tokens) {
   if (B < 1 || q_len < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || max_context_len < 1 || window < 0 ||
       split_tokens < 0)
     return 0;
-  if (Hq / Hkv * q_len > kMaxDecodeCols) return 0;  // prefill-kernel path: no workspace
-  return attn::plan_decode(B, q_len, Hq, Hkv, D, max_context_len, window, split_tokens)
+  // Wider than one tile: a bf16 cache takes the paged prefill kernel (no workspace), a byte cache
+  // the virtual KV heads; the size covers the latter, so it holds for either cache.
+  const int R = byte_cache_kv_rep(Hq / Hkv, q_len);
+  if (R == 0) return 0;
+  return attn::plan_decode(B, q_len, Hq, Hkv * R, D, max_context_len, window, split_tokens)
       .workspace_bytes;
 }
 
@@ -168,13 +181,17 @@ static int decode_impl(const char* who, const void* q, const void* k_cache, cons
   if (split_tokens % block_size != 0) return fail(ATTN_ERR_SHAPE, "split_tokens %d is not a multiple of block_size", split_tokens);
   if (split_tokens > attn::kMaxSplitTokens)
     return fail(ATTN_ERR_UNSUPPORTED, "split_tokens %d > %d", split_tokens, attn::kMaxSplitTokens);
-  if (Hq / Hkv * q_len > kMaxDecodeCols) {
-    // More query columns per KV head than one decode MFMA tile holds: the rows are a fixed-size
-    // chunk per sequence, computed by the paged prefill kernel (bf16 caches; it reads the cache
+  int kv_rep = 1;
+  if (Hq / Hkv * q_len > kMaxDecodeCols && kv_dtype != ATTN_BF16) {
+    // More query columns per KV head than one decode MFMA tile holds, byte cache: virtual KV
+    // heads, each cache head read once per virtual head
+    kv_rep = byte_cache_kv_rep(Hq / Hkv, q_len);
+    if (kv_rep == 0)
+      return fail(ATTN_ERR_UNSUPPORTED, "q_len %d > %d needs a bf16 cache", q_len, kMaxDecodeCols);
+  } else if (Hq / Hkv * q_len > kMaxDecodeCols) {
+    // More query columns per KV head than one decode MFMA tile holds, bf16 cache: the rows are a
+    // fixed-size chunk per sequence, computed by the paged prefill kernel (it reads the cache
     // through the same block table, K/V once per workgroup of query heads).
-    if (kv_dtype != ATTN_BF16)
-      return fail(ATTN_ERR_UNSUPPORTED, "(Hq/Hkv) * q_len = %d > %d needs a bf16 cache",
-                  Hq / Hkv * q_len, kMaxDecodeCols);
     if (B > 65535) return fail(ATTN_ERR_SHAPE, "B must be <= 65535");
     if ((long long)max_blocks_per_seq * block_size > 0x7fffffffLL)
       return fail(ATTN_ERR_SHAPE, "max_blocks_per_seq * block_size overflows int32");
@@ -190,9 +207,11 @@ static int decode_impl(const char* who, const void* q, const void* k_cache, cons
     attn::launch_prefill_paged(a, reinterpret_cast<hipStream_t>(stream));
     return check_launch(who);
   }
-  if (B > 65535 / q_len || Hkv > 65535) return fail(ATTN_ERR_SHAPE, "B * q_len and Hkv must be <= 65535");
+  if (B > 65535 / q_len || (long long)Hkv * kv_rep > 65535)
+    return fail(ATTN_ERR_SHAPE, "B * q_len and Hkv must be <= 65535");
+  const int Hkv_v = Hkv * kv_rep;  // virtual KV heads
   attn::DecodePlan plan =
-      attn::plan_decode(B, q_len, Hq, Hkv, D, max_context_len, window, split_tokens);
+      attn::plan_decode(B, q_len, Hq, Hkv_v, D, max_context_len, window, split_tokens);
   if (static_scratch) {
     // the partials go to this GPU's static scratch array instead of a caller workspace
     if (plan.workspace_bytes > attn::kNoAllocScratchBytes)
@@ -207,8 +226,8 @@ static int decode_impl(const char* who, const void* q, const void* k_cache, cons
     return fail(ATTN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", plan.workspace_bytes,
                 workspace ? workspace_bytes : (size_t)0);
   attn::DecodeArgs a{q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, o,
-                     kv_kind(kv_dtype), B, q_len, Hq, Hkv, D, block_size, max_blocks_per_seq,
-                     num_blocks, max_context_len, scale, window, plan, workspace};
+                     kv_kind(kv_dtype), B, q_len, Hq, Hkv_v, D, block_size, max_blocks_per_seq,
+                     num_blocks, max_context_len, scale, window, plan, workspace, kv_rep};
   attn::launch_decode(a, reinterpret_cast<hipStream_t>(stream));
   return check_launch(who);
 }

@@ -799,7 +799,9 @@ using DecodeWaveT = typename std::conditional<KV == kKvBf16 && GP < 8, DecodeWav
                                               DecodeWaveM<D, GP, KV>>::type;
 
 // ---- fixed split: one workgroup of 4 waves per (split, g, b) --------------------------------
-template <int D, int GP, int KV>
+// VIRT: g counts virtual KV heads, R of them per cache head (byte caches with more query columns
+// per cache head than one MFMA tile holds); without it R is 1 and not read.
+template <int D, int GP, int KV, bool VIRT>
 __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, const __half* __restrict__ k_scale,
@@ -807,7 +809,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     const int32_t* __restrict__ ctx_lens, uint16_t* __restrict__ out,
     float* __restrict__ part_o, float* __restrict__ part_lse, int Hq, int Hkv, int G, int QL,
     int max_blocks, int num_blocks, int max_ctx, float scale_log2, int window, int C,
-    int n_split) {
+    int n_split, int R) {
   using W = DecodeWaveT<D, GP, KV>;
   constexpr int BS = W::BS, U = W::U;
   // the V staging slices are dead once every wave has left its loop, and the per-wave O
@@ -823,6 +825,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
   // (dispatched round-robin over the XCDs) then belong to different sequences, so the XCDs
   // share ragged work evenly; splits that exist only for long contexts go first.
   const int split = n_split - 1 - blockIdx.z, g = blockIdx.x, b = blockIdx.y;
+  const int Hk = VIRT ? Hkv / R : Hkv, gk = VIRT ? g / R : g;  // the cache's heads, g's head
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -870,7 +873,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
       c.pb[u] = c.okb[u] ? e : 0;
     }
     c.t0 = t_begin + blk0 * BS;
-    w.load(c, k_cache, v_cache, k_scale, v_scale, Hkv, g, s_u.lds[wave]);
+    w.load(c, k_cache, v_cache, k_scale, v_scale, Hk, gk, s_u.lds[wave]);
   };
   for (int ch = wave; ch < nchunk; ch += kDecodeWaves) {
     prep(cA, ch);
@@ -986,7 +989,7 @@ __device__ __forceinline__ int visible_blocks(const int32_t* __restrict__ ctx_le
   return (ctx + 15) / 16 - first_key(ctx, QL, window) / 16;
 }
 
-template <int D, int GP, int KV>
+template <int D, int GP, int KV, bool VIRT>
 __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, const __half* __restrict__ k_scale,
@@ -994,7 +997,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
     const int32_t* __restrict__ ctx_lens, uint16_t* __restrict__ out,
     int32_t* __restrict__ prefix_out, float* __restrict__ part_o, float* __restrict__ part_lse,
     int B, int Hq, int Hkv, int G, int QL, int max_blocks, int num_blocks, int max_ctx,
-    float scale_log2) {
+    float scale_log2, int R) {
   using W = DecodeWaveT<D, GP, KV>;
   constexpr int BS = W::BS, U = W::U;
   constexpr int NSLOT = W::kMfmaPv ? 2 : 1;  // MFMA form: the next chunk's V lands in slot 1
@@ -1054,6 +1057,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
   }
   int nv = s_pre[b + 1] - s_pre[b];
   int g = (int)((pos0 - (int64_t)Hkv * s_pre[b]) / nv);
+  const int Hk = VIRT ? Hkv / R : Hkv;  // the cache's KV heads; virtual head g reads g / R
+  int gk = VIRT ? g / R : g;
 
   // Table entries of the wave's list range, 64 at a time: lane i of window k holds the entry
   // of list position pos0 + 64k + i. Windows are copied global -> LDS (two per wave) and the
@@ -1121,7 +1126,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
       c.pb[u] = c.okb[u] ? e : 0;
     }
     c.t0 = j * BS;
-    w.load(c, k_cache, v_cache, k_scale, v_scale, Hkv, g, s_lds[wave][slot]);
+    w.load(c, k_cache, v_cache, k_scale, v_scale, Hk, gk, s_lds[wave][slot]);
     if (W::kMfmaPv && ((++nchunk) & 3) == 0) {
       prio ^= 1;
       if (prio) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);
@@ -1166,6 +1171,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
         nv = s_pre[b + 1] - s_pre[b];
         ctx = decode_ctx(ctx_lens, b, max_ctx, max_blocks, BS);
       }
+      gk = VIRT ? g / R : g;
       seg0 = pend;
       pend = min(end, seg0 + nv);
       j0 = 0;
@@ -1317,9 +1323,9 @@ DecodePlan plan_decode(int B, int QL, int Hq, int Hkv, int D, int max_context_le
   return p;
 }
 
-template <int D, int GP, int KV>
+template <int D, int GP, int KV, bool VIRT>
 static void launch_stream(const DecodeArgs& a, hipStream_t stream) {
-  const auto kern = decode_stream_kernel<D, GP, KV>;
+  const auto kern = decode_stream_kernel<D, GP, KV, VIRT>;
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kDecodeThreads, 0) != hipSuccess ||
       per_cu < 1)
@@ -1334,26 +1340,26 @@ static void launch_stream(const DecodeArgs& a, hipStream_t stream) {
                      a.k_cache, a.v_cache, (const __half*)a.k_scale, (const __half*)a.v_scale,
                      a.block_table, a.context_lens, (uint16_t*)a.o, prefix, part_o, part_lse, a.B,
                      a.Hq, a.Hkv, G, a.q_len, a.max_blocks_per_seq, a.num_blocks,
-                     a.max_context_len, a.scale * kLog2e);
+                     a.max_context_len, a.scale * kLog2e, a.kv_rep);
   const int merge_wgs = (a.Hkv * G * a.q_len + kMergeCols - 1) / kMergeCols;
   hipLaunchKernelGGL(decode_stream_merge_kernel<D>, dim3(merge_wgs, a.B), dim3(64 * kMergeCols), 0,
                      stream, prefix, part_o, part_lse, (uint16_t*)a.o, a.B, a.Hq, a.Hkv, G,
                      a.q_len, wgs * kDecodeWaves);
 }
 
-template <int D, int GP, int KV>
+template <int D, int GP, int KV, bool VIRT>
 static void launch_split(const DecodeArgs& a, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
   const int C = a.plan.split_tokens, ns = a.plan.n_split;
   char* ws = reinterpret_cast<char*>(a.workspace);
   float* part_o = ns > 1 ? reinterpret_cast<float*>(ws + a.plan.part_o_off) : nullptr;
   float* part_lse = ns > 1 ? reinterpret_cast<float*>(ws + a.plan.part_lse_off) : nullptr;
-  hipLaunchKernelGGL((decode_split_kernel<D, GP, KV>), dim3(a.Hkv, a.B, ns), dim3(kDecodeThreads),
+  hipLaunchKernelGGL((decode_split_kernel<D, GP, KV, VIRT>), dim3(a.Hkv, a.B, ns), dim3(kDecodeThreads),
                      0, stream, (const uint16_t*)a.q, a.k_cache, a.v_cache,
                      (const __half*)a.k_scale, (const __half*)a.v_scale, a.block_table,
                      a.context_lens, (uint16_t*)a.o, part_o, part_lse, a.Hq, a.Hkv, G, a.q_len,
                      a.max_blocks_per_seq, a.num_blocks, a.max_context_len, a.scale * kLog2e,
-                     a.window, C, ns);
+                     a.window, C, ns, a.kv_rep);
   if (ns > 1)
     hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(a.Hq, a.B * a.q_len), dim3(64), 0, stream,
                        part_o, part_lse, a.context_lens, (uint16_t*)a.o, a.Hq, a.q_len,
@@ -1362,10 +1368,19 @@ static void launch_split(const DecodeArgs& a, hipStream_t stream) {
 
 template <int D, int GP, int KV>
 static void launch_shape(const DecodeArgs& a, hipStream_t stream) {
+  if constexpr (KV != kKvBf16) {
+    if (a.kv_rep > 1) {  // virtual KV heads (byte caches only)
+      if (a.plan.stream)
+        launch_stream<D, GP, KV, true>(a, stream);
+      else
+        launch_split<D, GP, KV, true>(a, stream);
+      return;
+    }
+  }
   if (a.plan.stream)
-    launch_stream<D, GP, KV>(a, stream);
+    launch_stream<D, GP, KV, false>(a, stream);
   else
-    launch_split<D, GP, KV>(a, stream);
+    launch_split<D, GP, KV, false>(a, stream);
 }
 
 template <int D, int KV>

@@ -48,11 +48,14 @@ struct DecodeArgs {
   const int32_t* context_lens;
   void* o;
   int kv;  // cache element kind: kKvBf16, kKvI8 or kKvFp8
+  // Hkv counts virtual KV heads: each of the cache's Hkv / kv_rep heads serves kv_rep of them,
+  // Hq / Hkv query heads each (kv_rep = 1: the cache's own heads)
   int B, q_len, Hq, Hkv, D, block_size, max_blocks_per_seq, num_blocks, max_context_len;
   float scale;
   int window;
   DecodePlan plan;
   void* workspace;
+  int kv_rep;
 };
 
 struct AppendArgs {

@@ -123,7 +123,9 @@ int attn_prefill_paged(const void* q, const void* k_new, const void* v_new, void
 
 /*
  * attn_decode_workspace_size -- bytes of device workspace attn_decode_paged needs for these
- * sizes (0 when the call runs as a single pass and needs none). split_tokens as below.
+ * sizes (0 when the call runs as a single pass and needs none). split_tokens as below. With
+ * more than 16 query heads per KV head the size is that of an INT8 / FP8 cache (virtual KV
+ * heads, below); a bf16 cache needs none of it there.
  */
 size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_context_len,
                                   int window, int split_tokens);
@@ -169,11 +171,14 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_context
  *  workspace    : device buffer of at least attn_decode_workspace_size(...) bytes (may be NULL
  *                 when that size is 0); overwritten by the call; its contents on entry do not
  *                 matter. Two calls in flight at once must not share a workspace.
- *  Requirements: D in {64, 128}; block_size == 16; Hq % Hkv == 0; Hq / Hkv <= 16 with an
- *                 INT8 or FP8 cache (ATTN_ERR_UNSUPPORTED above; a bf16 cache with more query
- *                 heads per KV head is computed by the paged prefill kernel, as in
- *                 attn_decode_paged_multi); q, o, k_cache, v_cache, k_scale and v_scale
- *                 16-byte aligned (else ATTN_ERR_SHAPE).
+ *  More than 16 query heads per KV head: a bf16 cache is read by the paged prefill kernel
+ *                 (as in attn_decode_paged_multi); an INT8 or FP8 cache by the decode kernels
+ *                 with virtual KV heads: each cache head is split into R groups of
+ *                 (Hq / Hkv) / R query heads, R the smallest divisor of Hq / Hkv that makes a
+ *                 group 16 heads or fewer, and read once per group (R times in all). The
+ *                 results equal those of a cache holding each head R times, bit for bit.
+ *  Requirements: D in {64, 128}; block_size == 16; Hq % Hkv == 0; q, o, k_cache, v_cache,
+ *                 k_scale and v_scale 16-byte aligned (else ATTN_ERR_SHAPE).
  */
 int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       const void* k_scale, const void* v_scale,
@@ -233,8 +238,12 @@ size_t attn_decode_multi_workspace_size(int B, int q_len, int Hq, int Hkv, int D
  *                 head) a bf16 cache is read by the paged prefill kernel instead (the rows of a
  *                 sequence as one fixed-size chunk, same row positions and zeros; no workspace,
  *                 split_tokens has no effect, context_lens is clamped to the table's capacity
- *                 only); an INT8 or FP8 cache returns ATTN_ERR_UNSUPPORTED there.
- *  workspace    : at least attn_decode_multi_workspace_size(...) bytes.
+ *                 only); an INT8 or FP8 cache by the decode kernels with virtual KV heads (as
+ *                 in attn_decode_paged: groups of (Hq / Hkv) / R heads with all q_len rows, at
+ *                 most 16 columns, each cache head read R times), which needs q_len <= 16
+ *                 (ATTN_ERR_UNSUPPORTED above).
+ *  workspace    : at least attn_decode_multi_workspace_size(...) bytes (for more than 16
+ *                 columns: the INT8 / FP8 need, which a bf16 cache does not use).
  * q_len == 1 computes exactly what attn_decode_paged computes.
  */
 int attn_decode_paged_multi(const void* q, const void* k_cache, const void* v_cache,

@@ -83,8 +83,8 @@ def _decode(**kw):
     (dict(ks=FAKE, vs=FAKE), A.ATTN_ERR_SHAPE), (dict(Hq=6, Hkv=4), A.ATTN_ERR_SHAPE),
     (dict(maxctx=0), A.ATTN_ERR_SHAPE), (dict(window=-2), A.ATTN_ERR_SHAPE), (dict(split=-16), A.ATTN_ERR_SHAPE),
     (dict(split=24), A.ATTN_ERR_SHAPE), (dict(D=80), A.ATTN_ERR_UNSUPPORTED), (dict(bs=8), A.ATTN_ERR_UNSUPPORTED),
-    # more than 16 query heads per KV head: only bf16 caches (through the prefill kernel)
-    (dict(Hq=34, Hkv=2, kv=A.ATTN_I8, ks=FAKE, vs=FAKE), A.ATTN_ERR_UNSUPPORTED),
+    # more than 16 query heads per KV head, byte cache: virtual KV heads, which stage partials
+    (dict(Hq=34, Hkv=2, kv=A.ATTN_I8, ks=FAKE, vs=FAKE), A.ATTN_ERR_WORKSPACE),
     (dict(split=8208), A.ATTN_ERR_UNSUPPORTED),
     (dict(maxctx=5000, split=64), A.ATTN_ERR_WORKSPACE),
     (dict(maxctx=5000, split=64, ws=FAKE, wsb=16), A.ATTN_ERR_WORKSPACE),
@@ -110,10 +110,13 @@ def _multi(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), A.ATTN_ERR_NULL), (dict(ql=0), A.ATTN_ERR_SHAPE), (dict(ql=-1), A.ATTN_ERR_SHAPE),
-    # 4 heads per KV head x 5 rows > 16 columns: a byte cache is refused (a bf16 cache goes
-    # through the prefill kernel)
-    (dict(ql=5, kv=A.ATTN_I8, ks=FAKE, vs=FAKE), A.ATTN_ERR_UNSUPPORTED),
-    (dict(Hq=16, Hkv=1, ql=2, kv=A.ATTN_FP8, ks=FAKE, vs=FAKE), A.ATTN_ERR_UNSUPPORTED),
+    # 4 heads per KV head x 5 rows > 16 columns, byte cache: virtual KV heads (one query head
+    # each), which stage partials; more than 16 rows: refused (a bf16 cache goes through the
+    # prefill kernel)
+    (dict(ql=5, kv=A.ATTN_I8, ks=FAKE, vs=FAKE), A.ATTN_ERR_WORKSPACE),
+    (dict(Hq=16, Hkv=1, ql=2, kv=A.ATTN_FP8, ks=FAKE, vs=FAKE), A.ATTN_ERR_WORKSPACE),
+    (dict(ql=17, kv=A.ATTN_I8, ks=FAKE, vs=FAKE), A.ATTN_ERR_UNSUPPORTED),
+    (dict(Hq=2, Hkv=2, ql=17, kv=A.ATTN_FP8, ks=FAKE, vs=FAKE), A.ATTN_ERR_UNSUPPORTED),
     (dict(ql=5, split=24), A.ATTN_ERR_SHAPE), (dict(ql=5, window=-1), A.ATTN_ERR_SHAPE),
     (dict(B=40000), A.ATTN_ERR_SHAPE), (dict(ql=5, B=70000), A.ATTN_ERR_SHAPE),
     (dict(), A.ATTN_ERR_WORKSPACE),                     # the balanced shape stages partials
@@ -123,13 +126,15 @@ def test_decode_multi_validation(kw, code):
     assert _multi(**kw) == code
 
 
-def test_wide_multi_row_decode_needs_no_workspace():
-    """More than 16 query columns per KV head run on the prefill kernel: no workspace."""
-    wm = A.attn_decode_multi_workspace_size
-    assert wm(3, 8, 32, 8, 64, 4096, 0, 0) == 0    # 4 heads x 8 rows
-    assert wm(3, 5, 20, 4, 128, 700, 100, 0) == 0  # 5 heads x 5 rows
-    assert A.attn_decode_workspace_size(3, 64, 2, 64, 4096, 0, 0) == 0  # 32 heads per KV head
-    assert wm(3, 4, 32, 8, 64, 4096, 0, 0) > 0     # 16 columns: the decode kernels
+def test_wide_decode_workspace_is_that_of_the_virtual_kv_heads():
+    """More than 16 query columns per KV head: the size is that of the byte-cache path, R
+    virtual KV heads per cache head (R the smallest divisor of Hq/Hkv that brings a virtual
+    head's columns to 16); a bf16 cache runs on the prefill kernel and needs none of it."""
+    wm, ws = A.attn_decode_multi_workspace_size, A.attn_decode_workspace_size
+    assert wm(3, 8, 32, 8, 64, 4096, 0, 0) == wm(3, 8, 32, 16, 64, 4096, 0, 0) > 0  # 4 x 8: R = 2
+    assert wm(3, 5, 20, 4, 128, 7000, 0, 0) == wm(3, 5, 20, 20, 128, 7000, 0, 0) > 0  # 5 x 5: R = 5
+    assert ws(3, 64, 2, 64, 4096, 0, 0) == ws(3, 64, 4, 64, 4096, 0, 0) > 0  # 32 heads: R = 2
+    assert wm(3, 17, 8, 8, 64, 4096, 0, 0) == 0  # 17 rows: no byte-cache path
 
 
 def test_multi_workspace_matches_single_row():

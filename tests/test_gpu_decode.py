@@ -72,6 +72,29 @@ def test_decode_int8_small(D, Hq, Hkv, window, split):
     assert maxabs(host_f64(o), ro) <= BF16_TOL
 
 
+@pytest.mark.parametrize("split", [0, 32])
+@pytest.mark.parametrize("D,Hq,Hkv,window", CASES[7:])
+def test_decode_int8_more_than_16_heads_per_kv_head(D, Hq, Hkv, window, split):
+    """32 and 20 query heads per KV head with an INT8 cache: virtual KV heads."""
+    test_decode_int8_small(D, Hq, Hkv, window, split)
+
+
+def test_int8_virtual_kv_heads_equal_a_cache_with_repeated_heads():
+    """Splitting each cache head into R virtual heads computes, for every query head, exactly
+    what a cache holding each head R times (and R times the KV heads) gives: bit for bit."""
+    import attention_attn_prefill_amd as A
+    wl, ctx, table, nb, qbits, qf = _small(64, 64, 2, 0, kv="i8")  # 32 heads per KV head: R = 2
+    kc, ks = int8_pool(wl, "k", nb)
+    vc, vs = int8_pool(wl, "v", nb)
+    rep = lambda x: np.repeat(x, 2, axis=1)  # [nb][Hkv][...] -> [nb][2 Hkv][...]
+    for split in (0, 32):
+        o = _decode(dev_bf16(qbits), dev(kc), dev(vc), dev(table), dev(ctx), wl, int(ctx.max()),
+                    ks=dev(ks), vs=dev(vs), split=split)
+        o2 = _decode(dev_bf16(qbits), dev(rep(kc)), dev(rep(vc)), dev(table), dev(ctx), wl,
+                     int(ctx.max()), ks=dev(rep(ks)), vs=dev(rep(vs)), split=split)
+        assert np.array_equal(host_bits(o), host_bits(o2)), split
+
+
 def test_ctx_one_returns_v_exactly():
     wl, ctx, table, nb, qbits, qf = _small(128, 16, 2, 0, ctx=(1, 1, 1))
     kb, vb = pool(wl, "k", nb), pool(wl, "v", nb)

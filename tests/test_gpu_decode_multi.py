@@ -62,6 +62,10 @@ CASES = [
     ((16, 50, 700), 6, 32, 8, 128, 0, "bf16"),
     ((300, 1500, 40), 8, 16, 4, 64, 100, "bf16"),
     ((20, 3000), 5, 20, 4, 64, 7, "bf16"),
+    # ... and with an INT8 cache: virtual KV heads (each cache head read once per virtual head)
+    ((9, 17, 100, 333, 2000), 8, 32, 8, 64, 0, "i8"),
+    ((16, 50, 700), 5, 20, 4, 128, 0, "i8"),
+    ((300, 1500, 40), 6, 24, 4, 128, 100, "i8"),
 ]
 
 

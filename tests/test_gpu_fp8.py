@@ -103,6 +103,20 @@ def test_fp8_decode_multi_rows():
     assert maxabs(host_f64(o).reshape(ro.shape), ro) <= BF16_TOL
 
 
+@pytest.mark.parametrize("QL,Hq,Hkv", [(8, 32, 8), (3, 48, 2)])
+def test_fp8_decode_multi_rows_more_than_16_columns(QL, Hq, Hkv):
+    """8 drafts x 4 heads and 3 drafts x 24 heads per KV head: virtual KV heads."""
+    import attention_attn_prefill_amd as A
+    wl, ctx, table, _, _, kc, ks, vc, vs = _small(128, Hq, Hkv, 0, (9, 200, 1500), 5310 + QL)
+    qb, qf = new_tokens(5311 + QL, len(ctx) * QL, Hq, 128, "k")
+    o = A.attn_decode_paged_multi(dev_bf16(qb.reshape(len(ctx), QL, Hq, 128)), dev(kc), dev(vc), dev(table),
+                                  dev(ctx), int(ctx.max()), k_scale=dev(ks), v_scale=dev(vs), scale=wl.scale)
+    torch().cuda.synchronize()
+    ro, _ = oracle.prefill_paged(qf, np.arange(len(ctx) + 1) * QL, oracle.dequantize_fp8(kc, ks),
+                                 oracle.dequantize_fp8(vc, vs), table, ctx, wl.scale, 16, True, 0)
+    assert maxabs(host_f64(o).reshape(ro.shape), ro) <= BF16_TOL
+
+
 def test_fp8_decode_70b_b16_sampled():
     """The INT8 70B-shaped configuration with an FP8 cache: quantized on the GPU (bit-exact
     on sampled blocks), decoded, and checked on sampled sequences."""

@@ -56,9 +56,18 @@ def _wide_decode_case(i):
                 spare=int(r.integers(0, 4)), seed=9300 + i)
 
 
+def _wide_byte_decode_case(i):
+    """The same widths with an INT8 or FP8 cache: virtual KV heads (each cache head split into
+    groups of query heads of at most 16 columns)."""
+    c = _wide_decode_case(10000 + i)
+    c["kv"] = "i8" if i % 2 == 0 else "fp8"
+    return c
+
+
 SCALE = max(1, int(os.environ.get("ATTN_RANDOM_SCALE", "1")))
 DECODE_CASES = [_decode_case(i) for i in range(60 * SCALE)] + \
-    [_wide_decode_case(i) for i in range(15 * SCALE)]
+    [_wide_decode_case(i) for i in range(15 * SCALE)] + \
+    [_wide_byte_decode_case(i) for i in range(10 * SCALE)]
 
 
 def _dec_id(c):
