@@ -118,11 +118,13 @@ int attn_prefill_paged(const void* q, const void* k_new, const void* v_new, void
 // query columns ((Hq / Hkv) * q_len) one decode wave holds: one MFMA tile
 constexpr int kMaxDecodeCols = 16;
 
-// More columns than that with an INT8 / FP8 cache: each cache head serves R virtual KV heads of
-// (Hq / Hkv) / R query heads, R the smallest divisor of Hq / Hkv that brings a virtual head's
-// columns to kMaxDecodeCols or fewer (the cache head is then read R times). 0: none exists
-// (q_len > kMaxDecodeCols).
-static int byte_cache_kv_rep(int G, int q_len) {
+// More columns than that: each cache head serves R virtual KV heads of (Hq / Hkv) / R query
+// heads, R the smallest divisor of Hq / Hkv that brings a virtual head's columns to
+// kMaxDecodeCols or fewer (the cache head is then read R times). 0: none exists
+// (q_len > kMaxDecodeCols). INT8 / FP8 caches always take this path; bf16 caches only at R = 2
+// (5 to 8 drafts at 4 query heads per KV head: ~100 against ~118 us on the paged prefill kernel,
+// which reads the cache once but fills a quarter of its rows; at R = 4, ~180 us).
+static int virtual_kv_rep(int G, int q_len) {
   for (int R = 1; R <= G; ++R)
     if (G % R == 0 && (G / R) * q_len <= kMaxDecodeCols) return R;
   return 0;
@@ -133,9 +135,9 @@ static size_t decode_workspace(int B, int q_len, int Hq, int Hkv, int D, int max
   if (B < 1 || q_len < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || max_context_len < 1 || window < 0 ||
       split_tokens < 0)
     return 0;
-  // Wider than one tile: a bf16 cache takes the paged prefill kernel (no workspace), a byte cache
-  // the virtual KV heads; the size covers the latter, so it holds for either cache.
-  const int R = byte_cache_kv_rep(Hq / Hkv, q_len);
+  // Wider than one tile: the virtual KV heads' size (a bf16 cache on the paged prefill kernel
+  // needs none of it), so it holds for either cache.
+  const int R = virtual_kv_rep(Hq / Hkv, q_len);
   if (R == 0) return 0;
   return attn::plan_decode(B, q_len, Hq, Hkv * R, D, max_context_len, window, split_tokens)
       .workspace_bytes;
@@ -182,16 +184,17 @@ static int decode_impl(const char* who, const void* q, const void* k_cache, cons
   if (split_tokens > attn::kMaxSplitTokens)
     return fail(ATTN_ERR_UNSUPPORTED, "split_tokens %d > %d", split_tokens, attn::kMaxSplitTokens);
   int kv_rep = 1;
-  if (Hq / Hkv * q_len > kMaxDecodeCols && kv_dtype != ATTN_BF16) {
-    // More query columns per KV head than one decode MFMA tile holds, byte cache: virtual KV
-    // heads, each cache head read once per virtual head
-    kv_rep = byte_cache_kv_rep(Hq / Hkv, q_len);
+  const int rep = Hq / Hkv * q_len > kMaxDecodeCols ? virtual_kv_rep(Hq / Hkv, q_len) : 1;
+  if (kv_dtype != ATTN_BF16 || rep == 2) {
+    // More query columns per KV head than one decode MFMA tile holds (INT8 / FP8 cache, or bf16
+    // at R = 2): virtual KV heads, each cache head read once per virtual head
+    kv_rep = rep;
     if (kv_rep == 0)
       return fail(ATTN_ERR_UNSUPPORTED, "q_len %d > %d needs a bf16 cache", q_len, kMaxDecodeCols);
   } else if (Hq / Hkv * q_len > kMaxDecodeCols) {
-    // More query columns per KV head than one decode MFMA tile holds, bf16 cache: the rows are a
-    // fixed-size chunk per sequence, computed by the paged prefill kernel (it reads the cache
-    // through the same block table, K/V once per workgroup of query heads).
+    // More query columns per KV head than one decode MFMA tile holds, bf16 cache, R != 2: the
+    // rows are a fixed-size chunk per sequence, computed by the paged prefill kernel (it reads
+    // the cache through the same block table, K/V once per workgroup of query heads).
     if (B > 65535) return fail(ATTN_ERR_SHAPE, "B must be <= 65535");
     if ((long long)max_blocks_per_seq * block_size > 0x7fffffffLL)
       return fail(ATTN_ERR_SHAPE, "max_blocks_per_seq * block_size overflows int32");

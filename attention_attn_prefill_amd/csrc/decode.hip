@@ -799,8 +799,8 @@ using DecodeWaveT = typename std::conditional<KV == kKvBf16 && GP < 8, DecodeWav
                                               DecodeWaveM<D, GP, KV>>::type;
 
 // ---- fixed split: one workgroup of 4 waves per (split, g, b) --------------------------------
-// VIRT: g counts virtual KV heads, R of them per cache head (byte caches with more query columns
-// per cache head than one MFMA tile holds); without it R is 1 and not read.
+// VIRT: g counts virtual KV heads, R of them per cache head (more query columns per cache head
+// than one MFMA tile holds); without it R is 1 and not read.
 template <int D, int GP, int KV, bool VIRT>
 __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ k_cache,
@@ -1368,14 +1368,12 @@ static void launch_split(const DecodeArgs& a, hipStream_t stream) {
 
 template <int D, int GP, int KV>
 static void launch_shape(const DecodeArgs& a, hipStream_t stream) {
-  if constexpr (KV != kKvBf16) {
-    if (a.kv_rep > 1) {  // virtual KV heads (byte caches only)
-      if (a.plan.stream)
-        launch_stream<D, GP, KV, true>(a, stream);
-      else
-        launch_split<D, GP, KV, true>(a, stream);
-      return;
-    }
+  if (a.kv_rep > 1) {  // virtual KV heads
+    if (a.plan.stream)
+      launch_stream<D, GP, KV, true>(a, stream);
+    else
+      launch_split<D, GP, KV, true>(a, stream);
+    return;
   }
   if (a.plan.stream)
     launch_stream<D, GP, KV, false>(a, stream);

@@ -21,7 +21,7 @@ per-call entry under `prefill` / `decode`. `--workload llama1b | swa | int8_70b 
 subsets (for profiling). Outside the timed steps, the default run also times
 attn_prefill_paged (chunked prefill over the paged cache with fused append: 4 sequences,
 1024-token chunks after 3072-token prefixes), attn_decode_paged_multi (4 and 8 draft rows per
-sequence on the Llama-shaped cache; 8 rows take the paged prefill kernel), kv_cache_append_rope
+sequence on the Llama-shaped cache; 8 rows run as two virtual KV heads per cache head), kv_cache_append_rope
 (a 64k-token prompt written into a
 paged cache with RoPE on K) and attn_decode_paged over an FP8 E4M3 copy of the Llama-shaped
 cache.
@@ -253,7 +253,12 @@ def time_decode_multi(t, A, dwl, Dd, reps: int, q_len: int = 4):
     # algorithmic bytes: the visible K/V once (as single-token decode) plus q_len x Q and O
     byts = decode_bytes(dwl, Dd["ctx_np"]) + 2.0 * dwl.B * (q_len - 1) * dwl.Hq * dwl.D * 2
     gbs = byts / (ms * 1e-3) / 1e9
-    path = "paged prefill kernel" if q_len * (dwl.Hq // dwl.Hkv) > 16 else "decode kernels"
+    G = dwl.Hq // dwl.Hkv
+    if q_len * G <= 16:
+        path = "decode kernels"
+    else:  # the library's routing: two virtual KV heads per cache head when that suffices
+        R = next((r for r in range(1, G + 1) if G % r == 0 and (G // r) * q_len <= 16), 0)
+        path = "decode kernels, 2 virtual KV heads per cache head" if R == 2 else "paged prefill kernel"
     return {"kernel": f"attn_decode_paged_multi ({path})", "q_len": q_len, "ms": ms,
             "ms_percentiles": _pct(per),
             "GB/s": gbs,
@@ -586,7 +591,7 @@ def main(argv=None):
         dwl, d3 = wls["decode_llama1b_b64"], Dd["decode_llama1b_b64"]
         out["prefill_paged"] = time_chunked(t, A, max(5, args.steps))
         out["decode_multi"] = time_decode_multi(t, A, dwl, d3, max(5, args.steps))
-        # 8 drafts: 32 query columns per KV head, computed by the paged prefill kernel
+        # 8 drafts: 32 query columns per KV head, two virtual KV heads of 16 columns each
         out["decode_multi_8"] = time_decode_multi(t, A, dwl, d3, max(5, args.steps), q_len=8)
         out["append_rope"] = time_append_rope(t, A, max(5, args.steps))
         out["decode_fp8"] = time_decode_fp8(t, A, dwl, d3, max(5, args.steps))

@@ -124,8 +124,8 @@ int attn_prefill_paged(const void* q, const void* k_new, const void* v_new, void
 /*
  * attn_decode_workspace_size -- bytes of device workspace attn_decode_paged needs for these
  * sizes (0 when the call runs as a single pass and needs none). split_tokens as below. With
- * more than 16 query heads per KV head the size is that of an INT8 / FP8 cache (virtual KV
- * heads, below); a bf16 cache needs none of it there.
+ * more than 16 query heads per KV head the size is that of the virtual KV heads (below),
+ * which a bf16 cache on the paged prefill kernel does not use.
  */
 size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_context_len,
                                   int window, int split_tokens);
@@ -171,12 +171,13 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_context
  *  workspace    : device buffer of at least attn_decode_workspace_size(...) bytes (may be NULL
  *                 when that size is 0); overwritten by the call; its contents on entry do not
  *                 matter. Two calls in flight at once must not share a workspace.
- *  More than 16 query heads per KV head: a bf16 cache is read by the paged prefill kernel
- *                 (as in attn_decode_paged_multi); an INT8 or FP8 cache by the decode kernels
- *                 with virtual KV heads: each cache head is split into R groups of
- *                 (Hq / Hkv) / R query heads, R the smallest divisor of Hq / Hkv that makes a
- *                 group 16 heads or fewer, and read once per group (R times in all). The
- *                 results equal those of a cache holding each head R times, bit for bit.
+ *  More than 16 query heads per KV head: virtual KV heads -- each cache head is split into R
+ *                 groups of (Hq / Hkv) / R query heads, R the smallest divisor of Hq / Hkv
+ *                 that makes a group 16 heads or fewer, and read by the decode kernels once
+ *                 per group (R times in all); the results equal those of a cache holding each
+ *                 head R times, bit for bit. An INT8 or FP8 cache always takes this path, a
+ *                 bf16 cache when R = 2; a bf16 cache with R > 2 is read once by the paged
+ *                 prefill kernel instead (as in attn_decode_paged_multi).
  *  Requirements: D in {64, 128}; block_size == 16; Hq % Hkv == 0; q, o, k_cache, v_cache,
  *                 k_scale and v_scale 16-byte aligned (else ATTN_ERR_SHAPE).
  */
@@ -235,15 +236,16 @@ size_t attn_decode_multi_workspace_size(int B, int q_len, int Hq, int Hkv, int D
  *  q_len        : >= 1. Up to (Hq / Hkv) * q_len = 16 query columns per KV head the rows and
  *                 heads share one MFMA tile of the decode kernels, so each K/V byte is read
  *                 once for all of them. Above 16 (e.g. 8 draft tokens at 4 query heads per KV
- *                 head) a bf16 cache is read by the paged prefill kernel instead (the rows of a
- *                 sequence as one fixed-size chunk, same row positions and zeros; no workspace,
- *                 split_tokens has no effect, context_lens is clamped to the table's capacity
- *                 only); an INT8 or FP8 cache by the decode kernels with virtual KV heads (as
- *                 in attn_decode_paged: groups of (Hq / Hkv) / R heads with all q_len rows, at
- *                 most 16 columns, each cache head read R times), which needs q_len <= 16
- *                 (ATTN_ERR_UNSUPPORTED above).
+ *                 head) the decode kernels run on virtual KV heads (as in attn_decode_paged:
+ *                 groups of (Hq / Hkv) / R heads with all q_len rows, at most 16 columns, each
+ *                 cache head read R times), which needs q_len <= 16 (ATTN_ERR_UNSUPPORTED above
+ *                 for an INT8 or FP8 cache). A bf16 cache takes that path when R = 2 (e.g. 5
+ *                 to 8 drafts at 4 query heads per KV head); otherwise it is read once by the
+ *                 paged prefill kernel (the rows of a sequence as one fixed-size chunk, same row
+ *                 positions and zeros; no workspace, split_tokens has no effect, context_lens is
+ *                 clamped to the table's capacity only).
  *  workspace    : at least attn_decode_multi_workspace_size(...) bytes (for more than 16
- *                 columns: the INT8 / FP8 need, which a bf16 cache does not use).
+ *                 columns: the virtual KV heads' need, unused on the paged prefill kernel).
  * q_len == 1 computes exactly what attn_decode_paged computes.
  */
 int attn_decode_paged_multi(const void* q, const void* k_cache, const void* v_cache,

@@ -43,8 +43,9 @@ def _poison_unused(pool_arr, table, ctx, bs=16, value=None):
 
 CASES = [(64, 8, 2, 0), (64, 32, 8, 5), (128, 8, 1, 0), (128, 4, 4, 40), (64, 16, 1, 0),
          (128, 64, 8, 0), (64, 6, 3, 17),
-         # more than 16 query heads per KV head: the paged prefill kernel's path
-         (64, 64, 2, 0), (128, 40, 2, 17)]
+         # more than 16 query heads per KV head: two virtual KV heads per cache head (bf16 and
+         # byte caches), three (byte caches; bf16 goes through the paged prefill kernel)
+         (64, 64, 2, 0), (128, 40, 2, 17), (64, 48, 1, 0)]
 
 
 @pytest.mark.parametrize("split", [0, 16, 48])
@@ -79,19 +80,25 @@ def test_decode_int8_more_than_16_heads_per_kv_head(D, Hq, Hkv, window, split):
     test_decode_int8_small(D, Hq, Hkv, window, split)
 
 
-def test_int8_virtual_kv_heads_equal_a_cache_with_repeated_heads():
+@pytest.mark.parametrize("kv", ["i8", "bf16"])
+def test_virtual_kv_heads_equal_a_cache_with_repeated_heads(kv):
     """Splitting each cache head into R virtual heads computes, for every query head, exactly
     what a cache holding each head R times (and R times the KV heads) gives: bit for bit."""
-    import attention_attn_prefill_amd as A
-    wl, ctx, table, nb, qbits, qf = _small(64, 64, 2, 0, kv="i8")  # 32 heads per KV head: R = 2
-    kc, ks = int8_pool(wl, "k", nb)
-    vc, vs = int8_pool(wl, "v", nb)
+    wl, ctx, table, nb, qbits, qf = _small(64, 64, 2, 0, kv=kv)  # 32 heads per KV head: R = 2
     rep = lambda x: np.repeat(x, 2, axis=1)  # [nb][Hkv][...] -> [nb][2 Hkv][...]
+    if kv == "i8":
+        (kc, ks), (vc, vs) = int8_pool(wl, "k", nb), int8_pool(wl, "v", nb)
+        put = dev
+    else:
+        kc, vc, ks, vs = pool(wl, "k", nb), pool(wl, "v", nb), None, None
+        put = dev_bf16
+    opt = lambda x: None if x is None else dev(x)
+    opt_rep = lambda x: None if x is None else dev(rep(x))
     for split in (0, 32):
-        o = _decode(dev_bf16(qbits), dev(kc), dev(vc), dev(table), dev(ctx), wl, int(ctx.max()),
-                    ks=dev(ks), vs=dev(vs), split=split)
-        o2 = _decode(dev_bf16(qbits), dev(rep(kc)), dev(rep(vc)), dev(table), dev(ctx), wl,
-                     int(ctx.max()), ks=dev(rep(ks)), vs=dev(rep(vs)), split=split)
+        o = _decode(dev_bf16(qbits), put(kc), put(vc), dev(table), dev(ctx), wl, int(ctx.max()),
+                    ks=opt(ks), vs=opt(vs), split=split)
+        o2 = _decode(dev_bf16(qbits), put(rep(kc)), put(rep(vc)), dev(table), dev(ctx), wl,
+                     int(ctx.max()), ks=opt_rep(ks), vs=opt_rep(vs), split=split)
         assert np.array_equal(host_bits(o), host_bits(o2)), split
 
 

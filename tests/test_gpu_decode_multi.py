@@ -57,11 +57,14 @@ CASES = [
     ((5, 800, 2100), 4, 32, 8, 128, 0, "i8"),
     ((33, 700), 2, 64, 8, 128, 64, "i8"),
     ((1, 2, 3), 1, 8, 2, 64, 0, "bf16"),
-    # more than 16 query columns per KV head (bf16): computed by the paged prefill kernel
-    ((9, 17, 100, 333, 2000), 8, 32, 8, 64, 0, "bf16"),
-    ((16, 50, 700), 6, 32, 8, 128, 0, "bf16"),
-    ((300, 1500, 40), 8, 16, 4, 64, 100, "bf16"),
-    ((20, 3000), 5, 20, 4, 64, 7, "bf16"),
+    # more than 16 query columns per KV head, bf16: virtual KV heads where two of them per cache
+    # head suffice, else the paged prefill kernel
+    ((9, 17, 100, 333, 2000), 8, 32, 8, 64, 0, "bf16"),   # 4 heads x 8 rows: R = 2
+    ((16, 50, 700), 6, 32, 8, 128, 0, "bf16"),            # R = 2
+    ((300, 1500, 40), 8, 16, 4, 64, 100, "bf16"),         # R = 2
+    ((20, 3000), 5, 20, 4, 64, 7, "bf16"),                # 5 heads x 5 rows: prefill kernel
+    ((13, 64, 1000, 129), 12, 16, 4, 64, 0, "bf16"),      # 4 heads x 12 rows: prefill kernel
+    ((300, 1500, 40), 9, 6, 2, 128, 100, "bf16"),         # 3 heads x 9 rows: prefill kernel
     # ... and with an INT8 cache: virtual KV heads (each cache head read once per virtual head)
     ((9, 17, 100, 333, 2000), 8, 32, 8, 64, 0, "i8"),
     ((16, 50, 700), 5, 20, 4, 128, 0, "i8"),
@@ -113,22 +116,23 @@ def test_decode_multi_rows_before_the_sequence_are_zero():
     assert maxabs(got[1], exp[0]) <= BF16_TOL
 
 
-def test_decode_multi_wide_rows_before_the_sequence_are_zero():
-    """The prefill-kernel path keeps the decode rows' meaning: with 8 rows against a 3-token
-    context, rows 0..4 sit at negative positions and are zeros; rows 5..7 sit at 0, 1, 2."""
-    c = _case((3, 40), 8, 32, 8, 64, seed=975)
+@pytest.mark.parametrize("QL", [8, 12])  # virtual KV heads (R = 2), the paged prefill kernel
+def test_decode_multi_wide_rows_before_the_sequence_are_zero(QL):
+    """Both wide paths keep the decode rows' meaning: with QL rows against a 3-token context,
+    rows 0..QL-4 sit at negative positions and are zeros; the last three sit at 0, 1, 2."""
+    c = _case((3, 40), QL, 32, 8, 64, seed=975 + QL)
     got = host_f64(_run(c))
-    assert (got[0, :5] == 0).all()
-    q0 = c["qf"].reshape(2, 8, *c["qf"].shape[1:])[0, 5:]
+    assert (got[0, :QL - 3] == 0).all()
+    q0 = c["qf"].reshape(2, QL, *c["qf"].shape[1:])[0, QL - 3:]
     o0, _ = oracle.prefill_paged(q0, np.array([0, 3]), c["kf"], c["vf"], c["table"][:1], c["ctx"][:1],
                                  c["wl"].scale, 16, True, 0)
-    assert maxabs(got[0, 5:], o0) <= BF16_TOL
+    assert maxabs(got[0, QL - 3:], o0) <= BF16_TOL
     assert maxabs(got[1], _expected(c, seqs=[1])[0]) <= BF16_TOL
 
 
 def test_decode_multi_llama1b_eight_drafts_sampled():
     """Llama-3.2-1B-shaped verification of 8 draft tokens (4 heads x 8 rows = 32 columns per KV
-    head, the paged prefill kernel's path): sampled sequences against the oracle."""
+    head: two virtual KV heads per cache head): sampled sequences against the oracle."""
     wl0 = DecodeWorkload("decode_llama1b_b64", 1003, "bf16", 64, 32, 8, 64, 512, 4096)
     ctx = context_lens(wl0)
     c = _case(tuple(int(x) for x in ctx), 8, 32, 8, 64, seed=1308, spare=0)
