@@ -1113,9 +1113,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
   w.init(lane);
   // MFMA form: the SIMD's issue arbiter favours older waves, so the workgroup dispatched first
   // on a CU streams faster than the second one (INT8 70B-shaped decode: ~161 against ~180 us to
-  // finish the same work). The second half of the grid (the later workgroups) starts at
-  // priority 1 and every wave flips its priority every 4 chunks, so the two classes alternate.
-  int prio = W::kMfmaPv && blockIdx.x >= gridDim.x / 2 ? 1 : 0, nchunk = 0;
+  // finish the same work). The second half of the grid (the later workgroups) holds priority 1
+  // for 3 of every 4 chunks, the first half for the remaining one: with equal shares (a flip
+  // every 4 chunks) the earlier workgroups still end ~7 us first; 3 of 4 (or 5 of 8) evens them
+  // out best (7 of 8 and always-high overshoot).
+  const bool late = blockIdx.x >= gridDim.x / 2;
+  int prio = W::kMfmaPv && late ? 1 : 0, nchunk = 0;
   if (prio) __builtin_amdgcn_s_setprio(1);
   typename W::Chunk cA;
   auto prep = [&](typename W::Chunk& c, int j, int slot) {
@@ -1127,9 +1130,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_stream_kernel(
     }
     c.t0 = j * BS;
     w.load(c, k_cache, v_cache, k_scale, v_scale, Hk, gk, s_lds[wave][slot]);
-    if (W::kMfmaPv && ((++nchunk) & 3) == 0) {
-      prio ^= 1;
-      if (prio) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);
+    if (W::kMfmaPv) {  // the later workgroups high for 3 chunks of 4, the earlier for 1 of 4
+      const int want = (((++nchunk) & 3) != 0) == late ? 1 : 0;
+      if (want != prio) {
+        prio = want;
+        if (prio) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);
+      }
     }
   };
 
