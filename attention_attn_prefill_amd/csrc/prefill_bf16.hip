@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kPrefillThreads, D == 128 ? 3 : 2) void prefill_bf1
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int S,
     int Hq, int Hkv, int G, int HW, int QW, int n_qblk, int n_hsub, float scale_log2,
-    int causal, int window, int cpx, PagedArgs pg) {
+    int causal, int window, int cpx, int gmajor, PagedArgs pg) {
   using T = PTile<D>;
   constexpr int kBN = T::BN;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -77,12 +77,16 @@ __global__ __launch_bounds__(kPrefillThreads, D == 128 ? 3 : 2) void prefill_bf1
   // ---- workgroup -> (b, kv head, head sub-group, query block) -----------------------------
   // Consecutive workgroup ids are dispatched round-robin over the 8 XCDs, each with its own L2.
   // When the number of (b, kv head, head sub-group) groups is a multiple of 8, group gi runs
-  // entirely on XCD gi % 8, so its K/V stream is fetched into one L2 and reused there; inside
-  // an XCD the query blocks go longest first, dealt to the XCD's CUs in rounds of `cpx` slots
-  // whose direction alternates (round r takes ranks rC .. rC+C-1 forwards when r is even,
-  // backwards when odd). When the whole grid is resident at once, the CU that receives the
-  // longest block of one round receives the shortest of the next, so every CU's causal work
-  // sums to about the same.
+  // entirely on XCD gi % 8, so its K/V stream is fetched into one L2 and reused there. An XCD
+  // holding several groups interleaves their query blocks when the whole grid is resident at
+  // once, and runs the groups one after the other (gmajor) when it is not, so that the keys its
+  // resident query blocks need at once are one group's band, not several (long-context window
+  // prefill: 2.05 -> 0.74 GB read per call, same time; with the grid resident, interleaving is
+  // 4 % faster on the chunked prefill). The query blocks go longest first, dealt to the XCD's
+  // CUs in rounds of `cpx` slots whose direction alternates (round r takes ranks rC .. rC+C-1
+  // forwards when r is even, backwards when odd). When the whole grid is resident at once, the
+  // CU that receives the longest block of one round receives the shortest of the next, so
+  // every CU's causal work sums to about the same.
   const int n_groups = gridDim.x / n_qblk;
   int gi, qblk_rank;
   if ((n_groups & 7) == 0) {
@@ -90,9 +94,14 @@ __global__ __launch_bounds__(kPrefillThreads, D == 128 ? 3 : 2) void prefill_bf1
     const int round = slot0 / cpx, pos = slot0 % cpx;
     const int len = min(cpx, (int)(gridDim.x >> 3) - round * cpx);  // last round may be short
     const int slot = round * cpx + ((round & 1) ? len - 1 - pos : pos);
-    const int per_xcd = n_groups >> 3;
-    qblk_rank = slot / per_xcd;
-    gi = xcd + 8 * (slot % per_xcd);
+    if (gmajor) {
+      qblk_rank = slot % n_qblk;
+      gi = xcd + 8 * (slot / n_qblk);
+    } else {
+      const int per_xcd = n_groups >> 3;
+      qblk_rank = slot / per_xcd;
+      gi = xcd + 8 * (slot % per_xcd);
+    }
   } else {
     qblk_rank = blockIdx.x % n_qblk;
     gi = blockIdx.x / n_qblk;
@@ -463,11 +472,24 @@ static void launch_d(const void* q, const void* k, const void* v, void* o, float
                                             hipFuncAttributeMaxDynamicSharedMemorySize,
                                             (int)lds) == hipSuccess,
                         std::memory_order_relaxed);
+  // workgroups resident per CU (queried once per device; 1 if the query fails)
+  static std::atomic<int> per_cu_cache[kMaxDevices];
+  int per_cu = per_cu_cache[dev].load(std::memory_order_relaxed);
+  if (per_cu == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prefill_bf16_kernel<D, PAGED>,
+                                                     kPrefillThreads, lds) != hipSuccess ||
+        per_cu < 1) {
+      (void)hipGetLastError();
+      per_cu = 1;
+    }
+    per_cu_cache[dev].store(per_cu, std::memory_order_relaxed);
+  }
   const int cus = device_cus();
+  const int gmajor = nwg > (long long)cus * per_cu ? 1 : 0;
   hipLaunchKernelGGL((prefill_bf16_kernel<D, PAGED>), dim3((unsigned)nwg), dim3(kPrefillThreads),
                      lds, stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                      (uint16_t*)o, lse, S, Hq, Hkv, G, HW, QW, n_qblk, n_hsub, scale_log2, causal,
-                     window, cus >= 16 ? cus / 8 : 1, pg);
+                     window, cus >= 16 ? cus / 8 : 1, gmajor, pg);
 }
 
 int launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
