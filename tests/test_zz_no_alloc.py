@@ -1,7 +1,7 @@
 """GPU check of attn_decode_paged_noalloc (through the C ABI): its output equals
 attn_decode_paged's bit for bit on the same inputs, on two calls in a row, the second with a
-smaller input (the static scratch keeps the first call's contents), and on a third call with an
-INT8 cache."""
+smaller input (the static scratch keeps the first call's contents), and on further calls with an
+INT8 cache (one of them with more than 16 query heads per KV head)."""
 import numpy as np
 import pytest
 
@@ -49,6 +49,10 @@ def test_noalloc_matches_workspace_entry_point():
     wl3, c3 = _case("na3", 3103, "i8", 3, 8, 1, 128, 100, 5000)
     ref3, got3 = _both(wl3, c3)
     assert np.array_equal(ref3, got3)
+    # fourth: an INT8 cache with 32 query heads per KV head (two virtual KV heads per cache head)
+    wl4, c4 = _case("na4", 3104, "i8", 6, 64, 2, 64, 50, 2000)
+    ref4, got4 = _both(wl4, c4)
+    assert np.array_equal(ref4, got4)
     # the first input again after the others: same bits as before
     _, again = _both(wl1, c1)
     assert np.array_equal(again, got1)
