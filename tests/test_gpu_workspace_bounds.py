@@ -3,7 +3,8 @@ workspace is exactly the size attn_decode_(multi_)workspace_size reports and the
 its shape, both carved out of larger buffers filled with a sentinel byte, which must be intact
 afterwards. Covers the balanced shape, fixed splits (window and explicit split_tokens),
 multi-row decode, virtual KV heads (INT8 and bf16) and the paged prefill kernel's path, and the
-contiguous prefill's O and LSE with ragged query tails."""
+contiguous prefill's O and LSE with ragged query tails, and kv_cache_append with table entries
+past the pool."""
 import numpy as np
 import pytest
 
@@ -87,3 +88,34 @@ def test_prefill_writes_stay_inside_out_and_lse(B, S, Hq, Hkv, D, window):
     t.cuda.synchronize()
     assert (o_buf[ob:] == SENTINEL).all().item() and (l_buf[lb:] == SENTINEL).all().item()
     assert t.isfinite(out.float()).all().item() and t.isfinite(lse).all().item()
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_append_writes_stay_inside_the_pool(int8):
+    """Rows whose table entry is past the pool (num_blocks, or any larger id), negative, or whose
+    position is past the table are skipped: nothing lands after the pool or its scales."""
+    import attention_attn_prefill_amd as A
+    t = torch()
+    Hkv, D, bs, nb = 2, 64, 16, 6
+    table = np.array([[0, 1, 2], [3, nb, 4], [5, nb + 7, -1]], np.int32)
+    seq = np.array([0, 0, 1, 1, 1, 2, 2, 2, 0], np.int32)
+    pos = np.array([0, 47, 5, 20, 40, 3, 17, 33, 48], np.int32)  # rows 3, 6, 7, 8 are skipped
+    kn, _ = new_tokens(8300 + int8, len(seq), Hkv, D, "k")
+    vn, _ = new_tokens(8310 + int8, len(seq), Hkv, D, "v")
+    esize = 1 if int8 else 2
+    cb = nb * Hkv * bs * D * esize
+    bufs = [_guarded(cb), _guarded(cb)]
+    dt = t.int8 if int8 else t.bfloat16
+    kc, vc = (b[:cb].view(dt).view(nb, Hkv, bs, D) for b in bufs)
+    kw = {}
+    if int8:
+        sb = nb * Hkv * bs * 2
+        sbufs = [_guarded(sb), _guarded(sb)]
+        kw = dict(k_scale=sbufs[0][:sb].view(t.float16).view(nb, Hkv, bs),
+                  v_scale=sbufs[1][:sb].view(t.float16).view(nb, Hkv, bs))
+        bufs += sbufs
+    A.kv_cache_append(dev_bf16(kn), dev_bf16(vn), dev(seq), dev(pos), dev(table), kc, vc, **kw)
+    t.cuda.synchronize()
+    sizes = [cb, cb] + ([sb, sb] if int8 else [])
+    for b, n in zip(bufs, sizes):
+        assert (b[n:] == SENTINEL).all().item()
