@@ -127,12 +127,23 @@ def test_prefill_paged_whole_sequence_equals_contiguous_prefill():
 
 def test_prefill_paged_llama1b_chunk_sampled():
     """Llama-3.2-1B-shaped chunked prefill: 4 sequences with 3072-token prefixes, 1024-token
-    chunks (4096 keys each), 32/8 heads, D = 64; sampled rows against the oracle."""
+    chunks (4096 keys each), 32/8 heads, D = 64; sampled rows against the oracle, every row
+    (O and LSE) of two (sequence, head) pairs on different KV heads, and the cache bits the
+    fused append wrote."""
     c = _case((4096,) * 4, (1024,) * 4, 32, 8, 64, seed=1234, spare=0)
-    o, L, kc, _ = _run(c, 0)
-    got = host_f64(o)
+    o, L, kc, vc = _run(c, 0)
+    got, gl = host_f64(o), host_f64(L)
     kexp = oracle.append_expected(bf16_value(c["kb"]), bf16_value(c["kn"]), c["seq"], c["pos"], c["table"], 16)
     vexp = oracle.append_expected(bf16_value(c["vb"]), bf16_value(c["vn"]), c["seq"], c["pos"], c["table"], 16)
+    assert np.array_equal(host_bits(kc), _bits(kexp)) and np.array_equal(host_bits(vc), _bits(vexp))
+    for b, h in ((1, 9), (2, 22)):
+        sel = np.arange(c["cu"][b], c["cu"][b + 1])
+        kk = oracle.gather_logical(kexp, c["table"][b], 4096, 16)
+        vv = oracle.gather_logical(vexp, c["table"][b], 4096, 16)
+        ro, rl = oracle.attention_head(bf16_value(c["qb"])[sel][:, h], kk[:, h // 4], vv[:, h // 4],
+                                       c["scale"], 3072 + np.arange(1024), True, 0)
+        assert maxabs(got[sel, h], ro) <= BF16_TOL
+        assert maxabs(gl[sel, h], rl) <= LSE_TOL_BF16
     rows = np.array([0, 1, 31, 32, 63, 64, 511, 1022, 1023])
     for b in (0, 3):
         sel = c["cu"][b] + rows
